@@ -1,0 +1,149 @@
+/*
+ * ffd.h -- C ABI of the FFD sparse decode-attention library (MI355X, gfx950).
+ *
+ * The method: "Faster Than Flash: Exploiting Attention Sparsity for Efficient
+ * Long-Context Decoding" (FFD). Cited below as
+ *   [TS]  the technical-summary page (gist.science) of that paper, by its
+ *         Methodology sections 1-3;
+ *   [AB]  the English abstract / "Key Innovations of FFD" on the
+ *         insight.aitobox.com blog page about the same paper.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor argument is a DEVICE pointer to contiguous row-major
+ *     memory that the caller allocated and owns. The library allocates
+ *     nothing, keeps no state except a per-thread error string, and never
+ *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL means
+ *     the default stream) and the call returns at once.
+ *   - bf16 tensors hold IEEE bfloat16 values (raw 16-bit patterns).
+ *   - A non-zero ffd_status means nothing was enqueued (argument errors) or
+ *     a launch failed (FFD_ERR_HIP); ffd_last_error() then describes it.
+ *   - Device-side values (sequence lengths, positions) are not validated;
+ *     out-of-range ones are clamped as documented per call.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef FFD_H
+#define FFD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FFD_ABI_VERSION 1
+
+typedef enum {
+  FFD_OK = 0,
+  FFD_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad scalar, misaligned pointer */
+  FFD_ERR_UNSUPPORTED = 2, /* valid request that the kernels do not implement (d, block size, G, S) */
+  FFD_ERR_WORKSPACE = 3,   /* workspace smaller than ffd_decode_workspace_bytes() */
+  FFD_ERR_HIP = 4          /* a HIP launch error */
+} ffd_status;
+
+typedef enum { FFD_OUT_BF16 = 0, FFD_OUT_F32 = 1 } ffd_out_dtype;
+
+/* Version of this ABI (FFD_ABI_VERSION). */
+int ffd_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). Host memory
+ * owned by the library, valid until the next library call on the thread. */
+const char* ffd_last_error(void);
+
+/*
+ * ffd_quantize_kv -- build or append the low-bit key sketch that the scan
+ * reads ([TS] Methodology 1: keys are kept in a low-bit form next to the
+ * full-precision cache and scanned instead of metadata indices; [AB]
+ * "content-aware scanning via low-bit quantization").
+ *
+ * For every sequence b, kv head j and token t in [pos_begin[b], pos_end[b])
+ * (clamped to [0, cap)), with k = K[b, j, t, :]:
+ *   amax = max_i |k_i|;  scale = fl32(amax / 7);  inv = fl32(7 / amax)
+ *   code_i = clamp(round_half_even(fl32(k_i * inv)), -7, 7)
+ *   (amax == 0: scale = 0 and every code 0)
+ * and stores kscale[b, j, t] = scale and the codes as two's-complement
+ * nibbles, element 2i in the low nibble of byte i of kq[b, j, t, :].
+ * Tokens outside the ranges are not touched.
+ *
+ *   k         bf16  [B, Hkv, cap, d]      input
+ *   kq        uint8 [B, Hkv, cap, d/2]    output (written for the range only)
+ *   kscale    f32   [B, Hkv, cap]         output (written for the range only)
+ *   pos_begin int32 [B]                   device; first token to (re)quantise
+ *   pos_end   int32 [B]                   device; one past the last
+ *   max_span  host int >= max_b (pos_end[b] - pos_begin[b]); sizes the grid,
+ *             tokens beyond pos_begin[b] + max_span are not processed
+ * Build a prefix with begin = 0, end = len; append one decoded token with
+ * begin = len - 1, end = len (after writing its bf16 K/V row). Both give the
+ * same bytes for the same token.
+ * Supported: d in {64, 128}. kq and k must be 16-byte aligned.
+ */
+ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale,
+                           const int32_t* pos_begin, const int32_t* pos_end,
+                           int B, int Hkv, int cap, int d, int max_span, void* stream);
+
+/* Bytes of scratch that ffd_decode needs for these sizes (per-split partial
+ * outputs and log-sum-exps, fp32). */
+size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int block_size,
+                                  int split_blocks);
+
+/*
+ * ffd_decode -- one FFD decode step: single-token attention of every query
+ * head over its sequence's KV cache, with the block selector and the
+ * attention computer fused ([TS] Methodology 3, "Fused Kernel": pseudo-max,
+ * Top-δ selection and fine-grained refinement in one kernel; [AB] "fully
+ * fused kernel").
+ *
+ * Query head h reads kv head h / (Hq / Hkv). For sequence b let
+ * L = clamp(seq_lens[b], 0, max_seq_len), NB = ceil(L / block_size). The
+ * blocks of a sequence are cut into splits of `split_blocks` consecutive
+ * blocks, one workgroup each. Per query head:
+ *   1. The query is quantised to int8 (scale fl32(amax/127), codes
+ *      clamp(rne(fl32(q_i * fl32(127/amax))), +-127)), cq = fl32(sq * sm_scale).
+ *   2. Scan ([TS] Methodology 3, "Top-δ Selection"): each valid token's
+ *      tentative score is fl32(float(dot) * fl32(kscale_t * cq)), dot being
+ *      the exact integer dot of the int8 query with the int4 codes; a block's
+ *      score is the max over its valid tokens.
+ *   3. Top-δ ([TS] Methodology 2, "Mechanism"): with m~ = the max block score
+ *      in the block's split, block j is kept iff score_j >= fl32(m~ - delta),
+ *      or j < sink_blocks, or j >= NB - local_blocks. δ is in natural-log
+ *      logit units ([TS] Methodology 2, "Adaptivity").
+ *   4. Refinement ([TS] Methodology 3, "Fine-Grained Refinement"): exact
+ *      softmax attention (logit = sm_scale * q.k on the bf16 values, fp32
+ *      accumulation) over the valid tokens of the kept blocks; per-split
+ *      partials are merged by a log-sum-exp combine.
+ * delta = +INFINITY selects the dense flash-decoding path: no scan, every
+ * valid block kept; kq and kscale may then be NULL.
+ *
+ *   q          bf16 [B, Hq, d]
+ *   k, v       bf16 [B, Hkv, cap, d]            rows >= L are never read
+ *   kq, kscale from ffd_quantize_kv over every valid token
+ *   seq_lens   int32 [B], device
+ *   max_seq_len host; bounds every L and sizes the grid and the mask
+ *   delta      >= 0 (fp32), +INFINITY allowed
+ *   sink_blocks, local_blocks >= 0
+ *   split_blocks in [1, 64]; part of the semantics (the kept set depends on it)
+ *   sm_scale   > 0 and finite (commonly fl32(1/sqrt(d)))
+ *   out        [B, Hq, d], bf16 (round half to even) or f32 per out_dtype
+ *   lse        f32 [B, Hq], natural log of the softmax normaliser over the
+ *              kept tokens of that head
+ *   kept_mask  uint8 [B, Hq, ceil(max_seq_len / block_size)] or NULL;
+ *              1 = kept, 0 = dropped or past NB
+ *   workspace  >= ffd_decode_workspace_bytes(B, Hq, d, max_seq_len,
+ *              block_size, split_blocks) bytes, 256-byte aligned
+ * A sequence with L == 0 gives out = 0, lse = -INFINITY and a zero mask row.
+ * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8}.
+ * q, k, v, kq must be 16-byte aligned.
+ */
+ffd_status ffd_decode(const void* q, const void* k, const void* v,
+                      const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
+                      int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
+                      int block_size, float delta, int sink_blocks, int local_blocks,
+                      int split_blocks, float sm_scale,
+                      void* out, int out_dtype, float* lse, uint8_t* kept_mask,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFD_H */

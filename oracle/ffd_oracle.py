@@ -52,6 +52,10 @@ import numpy as np
 F32 = np.float32
 KEY_QMAX = 7      # int4 symmetric range
 QUERY_QMAX = 127  # int8 symmetric range
+# Rows whose amax is below these powers of two are treated as all-zero: for
+# smaller amax, fl32(QMAX / amax) would overflow to +inf (and 0 * inf = NaN).
+KEY_TINY = np.float32(2.0 ** -125)
+QUERY_TINY = np.float32(2.0 ** -120)
 
 
 # --------------------------------------------------------------------------
@@ -72,12 +76,12 @@ def quantize_keys(k32: np.ndarray):
     """Quantise fp32 key rows ``[..., d]`` to int4 codes and one scale per row.
 
     amax = max_i |k_i|; scale = fl32(amax / 7); inv = fl32(7 / amax);
-    code_i = clamp(rne(fl32(k_i * inv)), -7, 7). A zero row gives scale 0 and
-    zero codes. Returns ``(codes int8 [..., d], scale float32 [...])``.
+    code_i = clamp(rne(fl32(k_i * inv)), -7, 7). A row with amax < 2^-125
+    (including an all-zero row) gives scale 0 and zero codes. Returns ``(codes int8 [..., d], scale float32 [...])``.
     """
     k32 = np.asarray(k32, dtype=np.float32)
     amax = np.max(np.abs(k32), axis=-1)
-    nz = amax > F32(0)
+    nz = amax >= KEY_TINY
     safe = np.where(nz, amax, F32(1)).astype(np.float32)
     inv = (F32(KEY_QMAX) / safe).astype(np.float32)
     scale = np.where(nz, (safe / F32(KEY_QMAX)).astype(np.float32), F32(0)).astype(np.float32)
@@ -114,11 +118,12 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
 def quantize_query(q32: np.ndarray, sm_scale) -> tuple:
     """int8 query for the scan. amax = max |q_i|; sq = fl32(amax/127);
     inv = fl32(127/amax); qc_i = clamp(rne(fl32(q_i*inv)), -127, 127);
-    cq = fl32(sq * sm_scale). A zero query gives qc = 0 and cq = 0."""
+    cq = fl32(sq * sm_scale). A query with amax < 2^-120 (including zero)
+    gives qc = 0 and cq = 0."""
     q32 = np.asarray(q32, dtype=np.float32)
     sm = F32(sm_scale)
     amax = F32(np.max(np.abs(q32)))
-    if amax == F32(0):
+    if not amax >= QUERY_TINY:
         return np.zeros(q32.shape, dtype=np.int8), F32(0)
     inv = F32(F32(QUERY_QMAX) / amax)
     sq = F32(amax / F32(QUERY_QMAX))
@@ -212,7 +217,7 @@ def select_head(q32: np.ndarray, codes: np.ndarray, scale: np.ndarray, k64: np.n
 
 
 def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink: int, local: int,
-           split_blocks: int, sm_scale=None, quantize: bool = True, heads=None):
+           split_blocks: int, sm_scale=None, quantize: bool = True, heads=None, mask_only: bool = False):
     """One FFD decode step.
 
     ``q`` bf16 bits ``[B, Hq, d]``; ``k``, ``v`` bf16 bits ``[B, Hkv, cap, d]``;
@@ -222,7 +227,8 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
     Returns ``(out fp64 [B,Hq,d], lse fp64 [B,Hq], mask uint8 [B,Hq,NB_max])``
     with ``NB_max = ceil(max_seq_len / block_size)``. A sequence with no valid
     token gives out 0, lse -inf and an all-zero mask row. ``heads`` restricts
-    the work to a list of ``(b, h)`` pairs (other rows are left NaN / 0).
+    the work to a list of ``(b, h)`` pairs (other rows are left NaN / 0);
+    ``mask_only`` skips the attention step (out and lse stay NaN).
     """
     q = np.asarray(q)
     B, Hq, d = q.shape
@@ -249,14 +255,16 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
                     lse[b, h] = -math.inf
                 continue
             k32 = bf16_bits_to_f32(k[b, j, :L])
-            k64 = k32.astype(np.float64)
-            v64 = bf16_bits_to_f32(v[b, j, :L]).astype(np.float64)
+            k64 = k32.astype(np.float64) if (not mask_only or not quantize) else None
+            v64 = None if mask_only else bf16_bits_to_f32(v[b, j, :L]).astype(np.float64)
             codes, scale = quantize_keys(k32) if quantize else (None, None)
             for h in hs:
                 q32 = bf16_bits_to_f32(q[b, h])
                 keep = select_head(q32, codes, scale, k64, L, block_size, delta, sink, local,
                                    split_blocks, sm_scale, quantize)
                 mask[b, h, :keep.shape[0]] = keep
+                if mask_only:
+                    continue
                 tok_keep = np.repeat(keep, block_size)[:L]
                 o, s = attend(q32.astype(np.float64), k64[tok_keep], v64[tok_keep], sm_scale)
                 out[b, h] = o

@@ -1,0 +1,27 @@
+"""FFD sparse decode attention for MI355X (gfx950).
+
+The hot path -- KV quantise/append, the fused scan -> Top-δ select -> attend
+decode kernel, and the split combine -- is hand-written HIP behind the C ABI
+in ``include/ffd.h`` (``libffd.so``, built in-tree). This package is its thin
+Python binding; PyTorch provides device memory and streams.
+"""
+
+from .ffd import (  # noqa: F401
+    EXPORTED_SYMBOLS,
+    FFD_ERR_HIP,
+    FFD_ERR_INVALID_ARG,
+    FFD_ERR_UNSUPPORTED,
+    FFD_ERR_WORKSPACE,
+    FFD_OK,
+    FFDError,
+    LIB_PATH,
+    alloc_workspace,
+    decode,
+    ffd_abi_version,
+    ffd_decode,
+    ffd_decode_workspace_bytes,
+    ffd_last_error,
+    ffd_quantize_kv,
+    lib,
+    quantize_kv,
+)

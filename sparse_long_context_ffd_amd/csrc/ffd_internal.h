@@ -1,0 +1,51 @@
+// Host-side declarations shared by the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ffd {
+
+constexpr int kBlockSize = 64;   // tokens per selection block
+constexpr int kMaxSplit = 64;    // max blocks per split (one workgroup)
+constexpr size_t kWsAlign = 256;
+
+struct DecodeParams {
+  const uint16_t* q;       // bf16 [B, Hq, D]
+  const uint16_t* k;       // bf16 [B, Hkv, cap, D]
+  const uint16_t* v;       // bf16 [B, Hkv, cap, D]
+  const uint8_t* kq;       // u8   [B, Hkv, cap, D/2]
+  const float* kscale;     // f32  [B, Hkv, cap]
+  const int32_t* seq_lens; // [B]
+  float* o_part;           // f32  [B, Hq, n_splits, D]   (normalised per split)
+  float* lse_part;         // f32  [B, Hq, n_splits]      (natural log)
+  uint8_t* mask;           // u8   [B, Hq, nb_max] or null
+  void* out;               // bf16 / f32 [B, Hq, D]
+  float* lse;              // f32 [B, Hq]
+  int out_f32;
+  int max_seq_len, B, Hq, Hkv, cap;
+  int nb_max;              // ceil(max_seq_len / kBlockSize)
+  int n_splits;            // ceil(nb_max / split_blocks)
+  int split_blocks;
+  int sink, local;
+  float delta, sm_scale;
+};
+
+// Workspace carving shared by sizing and launch.
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline size_t ws_opart_bytes(int B, int Hq, int n_splits, int D) {
+  return align_up((size_t)B * Hq * n_splits * D * sizeof(float), kWsAlign);
+}
+inline size_t ws_lse_bytes(int B, int Hq, int n_splits) {
+  return align_up((size_t)B * Hq * n_splits * sizeof(float), kWsAlign);
+}
+
+hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, const int32_t* pos_begin,
+                              const int32_t* pos_end, int B, int Hkv, int cap, int D, int max_span,
+                              hipStream_t stream);
+
+// Returns hipErrorInvalidValue for an unsupported (D, G) pair.
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, hipStream_t stream);
+
+}  // namespace ffd

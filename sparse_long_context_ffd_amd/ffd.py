@@ -1,0 +1,211 @@
+"""Python binding of ``libffd.so`` (ctypes).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI declared in ``include/ffd.h``. PyTorch supplies device
+memory and the current HIP stream. If the library has not been built this
+module raises on first use; there is no fallback.
+
+Low-level entry points keep the C names (``ffd_quantize_kv``, ``ffd_decode``,
+``ffd_decode_workspace_bytes``, ``ffd_last_error``, ``ffd_abi_version``) and
+take preallocated tensors. ``quantize_kv`` and ``decode`` are conveniences
+that allocate the outputs and the workspace with torch and then call them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libffd.so")
+
+FFD_OK = 0
+FFD_ERR_INVALID_ARG = 1
+FFD_ERR_UNSUPPORTED = 2
+FFD_ERR_WORKSPACE = 3
+FFD_ERR_HIP = 4
+FFD_OUT_BF16 = 0
+FFD_OUT_F32 = 1
+
+EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_decode_workspace_bytes",
+                    "ffd_decode")
+
+
+class FFDError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ffd status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib: Optional[ctypes.CDLL] = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libffd.so`` once; raises if it is missing (build it first)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FFDError(-1, f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python sparse_long_context_ffd_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    L.ffd_abi_version.restype = _i
+    L.ffd_abi_version.argtypes = []
+    L.ffd_last_error.restype = ctypes.c_char_p
+    L.ffd_last_error.argtypes = []
+    L.ffd_quantize_kv.restype = _i
+    L.ffd_quantize_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    L.ffd_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.ffd_decode_workspace_bytes.argtypes = [_i] * 6
+    L.ffd_decode.restype = _i
+    L.ffd_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,          # q k v kq kscale seq_lens
+                             _i, _i, _i, _i, _i, _i,                # max_seq_len B Hq Hkv d cap
+                             _i, ctypes.c_float, _i, _i, _i,        # block_size delta sink local split
+                             ctypes.c_float,                        # sm_scale
+                             _vp, _i, _vp, _vp,                     # out out_dtype lse mask
+                             _vp, ctypes.c_size_t, _vp]             # workspace bytes stream
+    _lib = L
+    return L
+
+
+def ffd_abi_version() -> int:
+    return lib().ffd_abi_version()
+
+
+def ffd_last_error() -> str:
+    return lib().ffd_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != FFD_OK:
+        raise FFDError(status, ffd_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if t.dtype != dtype or t.dim() != ndim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected a contiguous {ndim}-d {dtype} CUDA tensor, got "
+                         f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()} device={t.device}")
+
+
+def ffd_decode_workspace_bytes(B: int, Hq: int, d: int, max_seq_len: int, block_size: int = 64,
+                               split_blocks: int = 32) -> int:
+    return int(lib().ffd_decode_workspace_bytes(B, Hq, d, max_seq_len, block_size, split_blocks))
+
+
+def ffd_quantize_kv(k: torch.Tensor, kq: torch.Tensor, kscale: torch.Tensor, pos_begin: torch.Tensor,
+                    pos_end: torch.Tensor, max_span: int, stream=None) -> None:
+    """Quantise bf16 K rows ``[pos_begin[b], pos_end[b])`` into ``kq``/``kscale`` (in place)."""
+    _need(k, "k", torch.bfloat16, 4)
+    B, Hkv, cap, d = k.shape
+    _need(kq, "kq", torch.uint8, 4)
+    _need(kscale, "kscale", torch.float32, 3)
+    _need(pos_begin, "pos_begin", torch.int32, 1)
+    _need(pos_end, "pos_end", torch.int32, 1)
+    if tuple(kq.shape) != (B, Hkv, cap, d // 2) or tuple(kscale.shape) != (B, Hkv, cap):
+        raise ValueError("kq/kscale shapes do not match k")
+    if pos_begin.shape[0] != B or pos_end.shape[0] != B:
+        raise ValueError("pos_begin/pos_end need one entry per sequence")
+    _check(lib().ffd_quantize_kv(_ptr(k), _ptr(kq), _ptr(kscale), _ptr(pos_begin), _ptr(pos_end),
+                                 B, Hkv, cap, d, int(max_span), _stream(stream)))
+
+
+def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[torch.Tensor],
+               kscale: Optional[torch.Tensor], seq_lens: torch.Tensor, *, max_seq_len: int, block_size: int,
+               delta: float, sink: int, local: int, split_blocks: int, sm_scale: float, out: torch.Tensor,
+               lse: torch.Tensor, kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
+               stream=None) -> None:
+    """One decode step into preallocated ``out`` / ``lse`` / ``kept_mask``."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 4)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = k.shape
+    if tuple(k.shape) != (B, Hkv, cap, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k/v shapes do not match q")
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if kq is not None:
+        _need(kq, "kq", torch.uint8, 4)
+        _need(kscale, "kscale", torch.float32, 3)
+        if tuple(kq.shape) != (B, Hkv, cap, d // 2) or tuple(kscale.shape) != (B, Hkv, cap):
+            raise ValueError("kq/kscale shapes do not match k")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be bf16 or f32")
+    _need(out, "out", out.dtype, 3)
+    _need(lse, "lse", torch.float32, 2)
+    if tuple(out.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
+        raise ValueError("out/lse shapes")
+    if kept_mask is not None:
+        _need(kept_mask, "kept_mask", torch.uint8, 3)
+        if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
+            raise ValueError("kept_mask shape")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ffd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
+                            int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta), int(sink),
+                            int(local), int(split_blocks), float(sm_scale), _ptr(out),
+                            FFD_OUT_F32 if out.dtype == torch.float32 else FFD_OUT_BF16, _ptr(lse),
+                            _ptr(kept_mask), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# conveniences (allocate with torch, then call the C ABI)
+# ---------------------------------------------------------------------------
+
+def quantize_kv(k: torch.Tensor, seq_lens: torch.Tensor, kq: Optional[torch.Tensor] = None,
+                kscale: Optional[torch.Tensor] = None, max_span: Optional[int] = None, stream=None):
+    """Build the int4 sketch of ``k`` for tokens ``[0, seq_lens[b])``; returns ``(kq, kscale)``."""
+    B, Hkv, cap, d = k.shape
+    if kq is None:
+        kq = torch.zeros((B, Hkv, cap, d // 2), dtype=torch.uint8, device=k.device)
+    if kscale is None:
+        kscale = torch.zeros((B, Hkv, cap), dtype=torch.float32, device=k.device)
+    begin = torch.zeros(B, dtype=torch.int32, device=k.device)
+    end = seq_lens.to(device=k.device, dtype=torch.int32).contiguous()
+    span = cap if max_span is None else max_span
+    ffd_quantize_kv(k, kq, kscale, begin, end, span, stream)
+    return kq, kscale
+
+
+def alloc_workspace(B: int, Hq: int, d: int, max_seq_len: int, block_size: int = 64, split_blocks: int = 32,
+                    device="cuda") -> Optional[torch.Tensor]:
+    n = ffd_decode_workspace_bytes(B, Hq, d, max_seq_len, block_size, split_blocks)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode(q, k, v, kq, kscale, seq_lens, *, max_seq_len: Optional[int] = None, block_size: int = 64,
+           delta: float = 6.0, sink: int = 1, local: int = 4, split_blocks: int = 32,
+           sm_scale: Optional[float] = None, out_dtype=torch.bfloat16, with_mask: bool = True,
+           workspace: Optional[torch.Tensor] = None, stream=None):
+    """Allocate outputs and run one decode step; returns ``(out, lse, kept_mask)``."""
+    B, Hq, d = q.shape
+    if max_seq_len is None:
+        max_seq_len = k.shape[2]
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    nb_max = -(-max_seq_len // block_size)
+    mask = torch.empty((B, Hq, nb_max), dtype=torch.uint8, device=q.device) if with_mask else None
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, d, max_seq_len, block_size, split_blocks, q.device)
+    ffd_decode(q, k, v, kq, kscale, seq_lens, max_seq_len=max_seq_len, block_size=block_size, delta=delta,
+               sink=sink, local=local, split_blocks=split_blocks, sm_scale=sm_scale, out=out, lse=lse,
+               kept_mask=mask, workspace=workspace, stream=stream)
+    return out, lse, mask

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every entry point ``include/ffd.h``
+declares, and rejects bad arguments on the host before any GPU work."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_long_context_ffd_amd as ffd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "ffd.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ffd.lib()
+    names = _declared()
+    assert set(names) >= {"ffd_quantize_kv", "ffd_decode", "ffd_decode_workspace_bytes"}
+    for n in names:
+        assert hasattr(L, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", ffd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(ffd_[a-z_0-9]+)\b", dyn))
+    assert set(names) <= exported
+    assert set(ffd.EXPORTED_SYMBOLS) == set(names)
+    assert ffd.ffd_abi_version() == 1
+
+
+def test_workspace_bytes():
+    ns = -(-(-(-131072 // 64)) // 32)
+    exp = 4 * 32 * ns * 128 * 4 + (-(-4 * 32 * ns * 4 // 256)) * 256
+    assert ffd.ffd_decode_workspace_bytes(4, 32, 128, 131072, 64, 32) == exp
+    assert ffd.ffd_decode_workspace_bytes(4, 32, 128, 131072, 32, 32) == 0   # unsupported block size
+    assert ffd.ffd_decode_workspace_bytes(0, 32, 128, 131072, 64, 32) == 0
+
+
+def _decode(**kw):
+    args = dict(q=None, k=None, v=None, kq=None, kscale=None, seq_lens=None, max_seq_len=128, B=1, Hq=4, Hkv=1,
+                d=128, cap=128, block_size=64, delta=6.0, sink=1, local=4, split=32, sm_scale=0.088388,
+                out=None, out_dtype=0, lse=None, mask=None, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    L = ffd.lib()
+    return L.ffd_decode(args["q"], args["k"], args["v"], args["kq"], args["kscale"], args["seq_lens"],
+                        args["max_seq_len"], args["B"], args["Hq"], args["Hkv"], args["d"], args["cap"],
+                        args["block_size"], ctypes.c_float(args["delta"]), args["sink"], args["local"],
+                        args["split"], ctypes.c_float(args["sm_scale"]), args["out"], args["out_dtype"],
+                        args["lse"], args["mask"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Hq=6, Hkv=4), ffd.FFD_ERR_INVALID_ARG, "multiple"),
+    (dict(d=65), ffd.FFD_ERR_INVALID_ARG, "even"),
+    (dict(cap=64), ffd.FFD_ERR_INVALID_ARG, "cap"),
+    (dict(delta=-1.0), ffd.FFD_ERR_INVALID_ARG, "delta"),
+    (dict(delta=math.nan), ffd.FFD_ERR_INVALID_ARG, "delta"),
+    (dict(sink=-1), ffd.FFD_ERR_INVALID_ARG, "sink"),
+    (dict(split=0), ffd.FFD_ERR_INVALID_ARG, "split_blocks"),
+    (dict(sm_scale=0.0), ffd.FFD_ERR_INVALID_ARG, "sm_scale"),
+    (dict(sm_scale=math.inf), ffd.FFD_ERR_INVALID_ARG, "sm_scale"),
+    (dict(out_dtype=7), ffd.FFD_ERR_INVALID_ARG, "out_dtype"),
+    (dict(d=96), ffd.FFD_ERR_UNSUPPORTED, "d=96"),
+    (dict(block_size=32), ffd.FFD_ERR_UNSUPPORTED, "block_size"),
+    (dict(Hq=12, Hkv=4), ffd.FFD_ERR_UNSUPPORTED, "group size"),
+    (dict(split=65), ffd.FFD_ERR_UNSUPPORTED, "split_blocks"),
+    (dict(), ffd.FFD_ERR_INVALID_ARG, "null"),
+])
+def test_host_validation(kw, status, needle):
+    assert _decode(**kw) == status
+    assert needle in ffd.ffd_last_error()
+
+
+def test_workspace_too_small_and_misaligned():
+    fake = 1 << 20  # never dereferenced: validation fails before any launch
+    common = dict(q=fake, k=fake, v=fake, kq=fake, kscale=fake, seq_lens=fake, out=fake, lse=fake)
+    assert _decode(**common, ws=fake, ws_bytes=16) == ffd.FFD_ERR_WORKSPACE
+    assert "workspace" in ffd.ffd_last_error()
+    assert _decode(**common, ws=fake + 16, ws_bytes=1 << 30) == ffd.FFD_ERR_INVALID_ARG
+    assert "aligned" in ffd.ffd_last_error()
+    assert _decode(**{**common, "kq": None}, ws=fake, ws_bytes=1 << 30) == ffd.FFD_ERR_INVALID_ARG
+    assert "kq" in ffd.ffd_last_error()
+
+
+def test_empty_batch_is_a_no_op():
+    assert _decode(B=0) == ffd.FFD_OK
+    assert ffd.ffd_last_error() == ""
+    L = ffd.lib()
+    assert L.ffd_quantize_kv(None, None, None, None, None, 0, 8, 128, 128, 10, None) == ffd.FFD_OK
+    assert L.ffd_quantize_kv(None, None, None, None, None, 1, 8, 128, 96, 10, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert L.ffd_quantize_kv(None, None, None, None, None, 1, 8, 128, 128, 10, None) == ffd.FFD_ERR_INVALID_ARG

@@ -1,0 +1,52 @@
+"""Full-size workloads (128K x4, 256K, mixed 8K-128K x16) in the launch
+configuration the benchmark times: the whole kept-block mask bit-exact
+against the oracle, output and LSE on sampled heads (computed one by one)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import sparse_long_context_ffd_amd as ffd
+from ffd_inputs import WORKLOADS, make_inputs
+from oracle import ffd_oracle as O
+from tests.gpu_util import assert_close, assert_mask_equal, run_gpu, say, sm_scale_for, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_heads(w, mask, n=6, seed=0):
+    rng = np.random.default_rng(seed)
+    heads = {(int(rng.integers(w.B)), int(rng.integers(w.Hq))) for _ in range(n)}
+    # plus the head that drops the most blocks
+    kept = mask.sum(-1)
+    b, h = np.unravel_index(np.argmin(kept + (kept == 0) * 10 ** 9), kept.shape)
+    heads.add((int(b), int(h)))
+    return sorted(heads)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_128k_b4", "llama3_8b_256k", "mixed_16x8k_128k"])
+def test_full_size(name):
+    w = WORKLOADS[name]
+    say(f"full-size workload {name}: generating")
+    inp = make_inputs(w)
+    dv = to_device(inp)
+    sm = sm_scale_for(w.d)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    for delta in w.deltas:
+        say(f"  {name} delta={delta}: GPU")
+        out, lse, mask = run_gpu(dv, max_seq_len=inp["cap"], delta=delta, sink=w.sink, local=w.local,
+                                 split_blocks=w.split_blocks, sm_scale=sm, kq=kq, kscale=ks)
+        say(f"  kept fraction {mask[mask.sum(-1) > 0].mean() if mask.any() else 0:.4f}; oracle mask")
+        args = dict(max_seq_len=inp["cap"], block_size=64, delta=delta, sink=w.sink, local=w.local,
+                    split_blocks=w.split_blocks, sm_scale=np.float32(sm))
+        if not math.isinf(delta):
+            _, _, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], mask_only=True, **args)
+            assert_mask_equal(mask, r_mask, f"{name} mask delta={delta}")
+        heads = _sample_heads(w, mask, seed=int(delta) if math.isfinite(delta) else 99)
+        say(f"  oracle attention on heads {heads}")
+        r_out, r_lse, r_mask2 = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], heads=heads, **args)
+        for b, h in heads:
+            assert_mask_equal(mask[b, h], r_mask2[b, h], f"{name} mask b={b} h={h}")
+            assert_close(out[b, h], r_out[b, h], f"{name} out b={b} h={h} delta={delta}")
+            assert_close(lse[b, h], r_lse[b, h], f"{name} lse b={b} h={h} delta={delta}")

@@ -1,0 +1,123 @@
+"""ffd_decode on the GPU against the oracle: the kept-block mask bit-exact,
+output and LSE within 1e-3 + 2e-3*|ref|, on small ragged shapes that span
+several splits, and on the tiny and 32K workloads in full."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_long_context_ffd_amd as ffd
+from ffd_inputs import WORKLOADS, make_inputs, make_random_inputs
+from oracle import ffd_oracle as O
+from tests.gpu_util import assert_close, assert_mask_equal, run_gpu, say, sm_scale_for, to_device
+
+pytestmark = pytest.mark.gpu
+
+INF = math.inf
+
+# (B, Hq, Hkv, d, lens, delta, sink, local, S, extra)
+CASES = [
+    (1, 4, 1, 64, (2048,), 8.0, 1, 2, 32, {}),
+    (3, 8, 8, 128, (1, 63, 65), 2.0, 1, 1, 1, {}),
+    (2, 8, 4, 64, (64, 129), 0.0, 0, 0, 2, {}),
+    (2, 16, 2, 128, (4000, 1000), 1.0, 2, 3, 3, {}),
+    (4, 32, 8, 128, (0, 5000, 6400, 77), 6.0, 1, 4, 32, {}),
+    (1, 4, 1, 128, (8192,), 0.5, 0, 0, 64, {}),
+    (2, 16, 2, 64, (3000, 2999), INF, 1, 4, 32, {}),
+    (1, 8, 2, 128, (300,), 0.0, 3, 3, 2, {}),
+    (1, 4, 2, 128, (5000,), 3.0, 1, 2, 5, {"max_seq_len": 3000}),
+    (2, 8, 2, 128, (700, 1500), 1.5, 1, 1, 7, {"out_dtype": torch.float32}),
+    (1, 2, 1, 64, (4097,), 0.25, 0, 1, 64, {}),
+    (1, 4, 4, 128, (64 * 64 + 1,), 4.0, 1, 1, 64, {}),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_small_cases(case):
+    B, Hq, Hkv, d, lens, delta, sink, local, S, extra = CASES[case]
+    say(f"decode case {case}: B={B} Hq={Hq} Hkv={Hkv} d={d} lens={lens} delta={delta} S={S} {extra}")
+    inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=100 + case, block_size=64, hot_frac=0.05)
+    msl = extra.get("max_seq_len", inp["cap"])
+    sm = sm_scale_for(d)
+    dv = to_device(inp)
+    out, lse, mask = run_gpu(dv, max_seq_len=msl, delta=delta, sink=sink, local=local, split_blocks=S,
+                             sm_scale=sm, out_dtype=extra.get("out_dtype", torch.bfloat16))
+    r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=msl,
+                                    block_size=64, delta=delta, sink=sink, local=local, split_blocks=S,
+                                    sm_scale=np.float32(sm))
+    assert_mask_equal(mask, r_mask, "mask")
+    assert_close(out, r_out, "out")
+    assert_close(lse, r_lse, "lse")
+
+
+def test_tiny_workload_and_dense_limit():
+    w = WORKLOADS["tiny_d64_2k"]
+    say(f"decode workload {w.name}")
+    inp = make_inputs(w, poison_tail=True)
+    dv = to_device(inp)
+    sm = sm_scale_for(w.d)
+    for delta in w.deltas:
+        out, lse, mask = run_gpu(dv, max_seq_len=inp["cap"], delta=delta, sink=w.sink, local=w.local,
+                                 split_blocks=w.split_blocks, sm_scale=sm)
+        r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
+                                        block_size=64, delta=delta, sink=w.sink, local=w.local,
+                                        split_blocks=w.split_blocks, sm_scale=np.float32(sm))
+        assert_mask_equal(mask, r_mask, f"mask delta={delta}")
+        assert_close(out, r_out, f"out delta={delta}")
+        assert_close(lse, r_lse, f"lse delta={delta}")
+        if math.isinf(delta):
+            d_out, d_lse, _ = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
+                                       block_size=64, delta=INF, sink=0, local=0, split_blocks=32,
+                                       sm_scale=np.float32(sm), quantize=False)
+            assert mask.all()
+            assert_close(out, d_out, "dense out")
+            assert_close(lse, d_lse, "dense lse")
+
+
+def test_32k_workload():
+    w = WORKLOADS["llama3_8b_32k"]
+    say(f"decode workload {w.name}")
+    inp = make_inputs(w, poison_tail=True)
+    dv = to_device(inp)
+    sm = sm_scale_for(w.d)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    for delta in w.deltas:
+        out, lse, mask = run_gpu(dv, max_seq_len=inp["cap"], delta=delta, sink=w.sink, local=w.local,
+                                 split_blocks=w.split_blocks, sm_scale=sm, kq=kq, kscale=ks)
+        r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
+                                        block_size=64, delta=delta, sink=w.sink, local=w.local,
+                                        split_blocks=w.split_blocks, sm_scale=np.float32(sm))
+        say(f"  delta={delta}: kept fraction {mask.mean():.4f}")
+        assert_mask_equal(mask, r_mask, f"mask delta={delta}")
+        assert_close(out, r_out, f"out delta={delta}")
+        assert_close(lse, r_lse, f"lse delta={delta}")
+
+
+def test_deterministic():
+    say("decode determinism")
+    inp = make_random_inputs(2, 32, 8, 128, (9000, 4000), seed=77, block_size=64)
+    dv = to_device(inp)
+    res = [run_gpu(dv, max_seq_len=inp["cap"], delta=2.0, sink=1, local=4, split_blocks=32,
+                   sm_scale=sm_scale_for(128)) for _ in range(2)]
+    for a, b in zip(res[0], res[1]):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_no_mask_pointer_and_reused_workspace():
+    say("decode without mask, shared workspace")
+    inp = make_random_inputs(1, 8, 2, 128, (3000,), seed=5, block_size=64)
+    dv = to_device(inp)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    ws = ffd.alloc_workspace(1, 8, 128, inp["cap"], 64, 16)
+    a = ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], delta=1.0, split_blocks=16, workspace=ws)
+    b = ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], delta=1.0, split_blocks=16, workspace=ws,
+                   with_mask=False)
+    torch.cuda.synchronize()
+    assert b[2] is None
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    with pytest.raises(ffd.FFDError) as ei:
+        ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], delta=1.0, split_blocks=16,
+                   workspace=ws[:100])
+    assert ei.value.status == ffd.FFD_ERR_WORKSPACE

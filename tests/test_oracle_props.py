@@ -224,3 +224,18 @@ def test_lse_merge_of_a_partition_equals_single_pass(seed, cut):
     o1k, s1k = O.attend(q, k[:1], v[:1], 0.7)
     np.testing.assert_allclose(o1k, v[0], atol=1e-15)
     assert abs(s1k - 0.7 * float(k[0] @ q)) < 1e-12
+
+
+def test_tiny_rows_are_zero_rows():
+    """Rows whose amax is too small for fl32(QMAX/amax) to stay finite are zero rows."""
+    tiny = np.float32(2.0 ** -126)
+    ok = np.float32(2.0 ** -125)
+    k = np.array([[tiny, -tiny / 2, 0, 0], [ok, -ok, 0, ok / 2]], np.float32)
+    codes, scale = O.quantize_keys(k)
+    assert (codes[0] == 0).all() and scale[0] == 0
+    assert codes[1].tolist() == [7, -7, 0, 4] and np.isfinite(np.float32(7) / ok)
+    assert scale[1] == np.float32(ok / np.float32(7))
+    qc, cq = O.quantize_query(np.array([2.0 ** -121, 0], np.float32), np.float32(1))
+    assert (qc == 0).all() and cq == 0
+    qc, cq = O.quantize_query(np.array([2.0 ** -120, 0], np.float32), np.float32(1))
+    assert qc.tolist() == [127, 0] and cq > 0

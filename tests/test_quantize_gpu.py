@@ -1,0 +1,74 @@
+"""ffd_quantize_kv on the GPU is bit-identical to the oracle's int4 quantiser."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_long_context_ffd_amd as ffd
+from ffd_inputs import bf16_bits_from_f32, make_random_inputs
+from oracle import ffd_oracle as O
+from tests.gpu_util import dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B,Hkv,d,lens,seed", [
+    (1, 1, 64, (2048,), 1),
+    (2, 3, 128, (1000, 77), 2),
+    (3, 2, 64, (1, 0, 130), 3),
+    (1, 8, 128, (4096,), 4),
+])
+def test_build_is_bit_exact(B, Hkv, d, lens, seed):
+    say(f"quantize build B={B} Hkv={Hkv} d={d} lens={lens}")
+    inp = make_random_inputs(B, Hkv, Hkv, d, lens, seed=seed, block_size=64, hot_frac=0.1)
+    k = dev_bf16(inp["k"])
+    seq = torch.tensor(inp["seq_lens"], dtype=torch.int32, device="cuda")
+    kq = torch.full((B, Hkv, inp["cap"], d // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    ks = torch.full((B, Hkv, inp["cap"]), -1.0, dtype=torch.float32, device="cuda")
+    ffd.quantize_kv(k, seq, kq=kq, kscale=ks)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_cache(inp["k"], inp["seq_lens"])
+    gq, gs = kq.cpu().numpy(), ks.cpu().numpy()
+    for b, L in enumerate(inp["seq_lens"]):
+        np.testing.assert_array_equal(gq[b, :, :L], rq[b, :, :L])
+        np.testing.assert_array_equal(gs[b, :, :L].view(np.uint32), rs[b, :, :L].view(np.uint32))
+        assert (gq[b, :, L:] == 0xAB).all() and (gs[b, :, L:] == -1.0).all()   # untouched
+
+
+def test_special_rows():
+    say("quantize special rows")
+    d = 128
+    rng = np.random.default_rng(5)
+    rows = [np.zeros(d), rng.standard_normal(d) * 1e-30, rng.standard_normal(d) * 1e30,
+            np.full(d, 2.0 ** -126), np.full(d, 2.0 ** -125), np.r_[np.full(d - 1, 1e-40), 1.0],
+            np.arange(d) - 63.5, np.where(np.arange(d) % 2, 3.5, -0.25), rng.standard_normal(d)]
+    rows += [rng.standard_normal(d) * 10.0 ** rng.integers(-20, 20) for _ in range(55)]
+    k32 = np.stack(rows).astype(np.float32)
+    kb = bf16_bits_from_f32(k32)[None, None]
+    L = kb.shape[2]
+    k = dev_bf16(kb)
+    seq = torch.tensor([L], dtype=torch.int32, device="cuda")
+    kq, ks = ffd.quantize_kv(k, seq)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_cache(kb, [L])
+    np.testing.assert_array_equal(kq.cpu().numpy(), rq)
+    np.testing.assert_array_equal(ks.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_append_equals_build():
+    say("quantize append == build")
+    inp = make_random_inputs(2, 4, 4, 128, (300, 130), seed=9, block_size=64)
+    k = dev_bf16(inp["k"])
+    B, Hkv, cap, d = k.shape
+    full = torch.tensor(inp["seq_lens"], dtype=torch.int32, device="cuda")
+    kq_a, ks_a = ffd.quantize_kv(k, full)
+    kq_b = torch.zeros_like(kq_a)
+    ks_b = torch.zeros_like(ks_a)
+    prefix = full - 5
+    ffd.quantize_kv(k, prefix, kq=kq_b, kscale=ks_b)
+    for step in range(5):   # append one token at a time
+        begin = prefix + step
+        ffd.ffd_quantize_kv(k, kq_b, ks_b, begin.contiguous(), (begin + 1).contiguous(), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(kq_a, kq_b)
+    assert torch.equal(ks_a.view(torch.int32), ks_b.view(torch.int32))
