@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""FFD decode benchmark on one MI355X.
+
+One step = one decode step of the whole batch: the fused scan -> Top-δ select
+-> attend kernel (``ffd_decode_partials``) plus the split combine
+(``ffd_combine``). Inputs (bf16 q/K/V, the int4 key sketch) are built and
+resident in HBM before timing starts. Prints ONE JSON line.
+
+Effective bandwidth counts algorithmic bytes: 68 B per valid token per kv
+head for the int4 scan (64 B codes + 4 B scale at d=128) plus 512 B (bf16 K
+and V rows) per valid token of every block kept by at least one query head
+of its group; the dense path (delta = inf) counts the 512 B only.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--delta D]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, vendor datasheet
+METRIC = "sparse decode-attention µs/step + effective HBM GB/s at 128K context"
+DEFAULT_WORKLOAD = "llama3_8b_128k_b4"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+DECODE_SOURCES = ["ffd_decode.hip", "ffd_device.h", "ffd_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "sparse_long_context_ffd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def algorithmic_bytes(mask, seq_lens, Hkv: int, G: int, d: int, bs: int, dense: bool):
+    """Bytes the method must move for one step, from the kept-block mask."""
+    import numpy as np
+
+    B = mask.shape[0]
+    scan_tok = d // 2 + 4
+    kv_tok = 2 * d * 2
+    scan = 0
+    kv = 0
+    kept_union = 0
+    blocks = 0
+    for b in range(B):
+        L = int(seq_lens[b])
+        nb = -(-L // bs)
+        if nb == 0:
+            continue
+        valid = np.full(nb, bs, dtype=np.int64)
+        valid[-1] = L - (nb - 1) * bs
+        for j in range(Hkv):
+            union = mask[b, j * G:(j + 1) * G, :nb].any(axis=0)
+            kv += int(valid[union].sum()) * kv_tok
+            kept_union += int(union.sum())
+            blocks += nb
+            if not dense:
+                scan += L * scan_tok
+    return scan, kv, (kept_union / blocks if blocks else 0.0)
+
+
+def load_traffic(workload: str, delta: float, launches_bytes: float):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"fused_decode_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if rec.get("delta") != (None if math.isinf(delta) else delta):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same step: query
+    heads of sequence 0, whole kv-head groups at a time, until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ffd_oracle as O
+
+    G = w.Hq // w.Hkv
+    done_heads = []
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        for j in range(w.Hkv):
+            heads = [(0, h) for h in range(j * G, (j + 1) * G)]
+            t0 = time.perf_counter()
+            O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"], block_size=w.block_size,
+                     delta=delta, sink=w.sink, local=w.local, split_blocks=w.split_blocks,
+                     sm_scale=np.float32(sm_scale), heads=heads)
+            t_total += time.perf_counter() - t0
+            done_heads += heads
+            if t_total >= budget_s:
+                break
+    return t_total, done_heads
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--delta", type=float, default=None, help="default: the workload's first delta")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the delta=inf comparison")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB read+write elementwise kernel (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the decode path has no multi-GPU mode here.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import sparse_long_context_ffd_amd as ffd
+    from ffd_inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe:
+        n = 1 << 29   # bf16 elements = 1 GiB read + 1 GiB written per launch
+        a = torch.randn(n, device=dev).to(torch.bfloat16)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n, "launches": 5}))
+        return 0
+
+    w = WORKLOADS[args.workload]
+    delta = w.deltas[0] if args.delta is None else args.delta
+    dense = math.isinf(delta)
+    G = w.Hq // w.Hkv
+    sm_scale = float(np.float32(1.0 / math.sqrt(w.d)))
+
+    t0 = time.perf_counter()
+    inp = make_inputs(w)
+    gen_s = time.perf_counter() - t0
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf16(inp["q"]), bf16(inp["k"]), bf16(inp["v"])
+    seq = torch.from_numpy(inp["seq_lens"]).to(dev)
+    B, Hkv, cap, d = k.shape
+    msl = cap
+    kq = torch.zeros((B, Hkv, cap, d // 2), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((B, Hkv, cap), dtype=torch.float32, device=dev)
+    begin = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    # quantised-cache build, timed on its own (not part of a decode step)
+    qb0, qb1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ffd.ffd_quantize_kv(k, kq, ks, begin, seq, cap)
+    qb0.record()
+    ffd.ffd_quantize_kv(k, kq, ks, begin, seq, cap)
+    qb1.record()
+    torch.cuda.synchronize()
+    quant_build_us = qb0.elapsed_time(qb1) * 1e3
+
+    out = torch.empty((B, w.Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, w.Hq), dtype=torch.float32, device=dev)
+    nb_max = -(-msl // w.block_size)
+    mask = torch.empty((B, w.Hq, nb_max), dtype=torch.uint8, device=dev)
+    ws = ffd.alloc_workspace(B, w.Hq, d, msl, w.block_size, w.split_blocks, dev)
+    kw = dict(max_seq_len=msl, block_size=w.block_size, split_blocks=w.split_blocks)
+
+    def step(dl, ev=None):
+        if ev is not None:
+            ev[0].record()
+        ffd.ffd_decode_partials(q, k, v, None if math.isinf(dl) else kq, None if math.isinf(dl) else ks, seq,
+                                delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale, kept_mask=mask,
+                                workspace=ws, **kw)
+        if ev is not None:
+            ev[1].record()
+        ffd.ffd_combine(seq, workspace=ws, out=out, lse=lse, **kw)
+        if ev is not None:
+            ev[2].record()
+
+    def timed(dl, steps, warmup):
+        for _ in range(warmup):
+            step(dl)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_a = time.perf_counter()
+        for i in range(steps):
+            step(dl, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_a
+        fused = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
+        comb = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
+        return wall, fused, comb
+
+    wall, fused_us, comb_us = timed(delta, args.steps, args.warmup)
+    step_us_wall = wall / args.steps * 1e6
+    m = mask.cpu().numpy()
+    scan_b, kv_b, union_keep = algorithmic_bytes(m, inp["seq_lens"], Hkv, G, d, w.block_size, dense)
+    alg_bytes = scan_b + kv_b
+    head_keep = float(m[:, :, :].sum() / max(1, sum(-(-int(L) // w.block_size) for L in inp["seq_lens"]) * w.Hq))
+    fused_avg = float(fused_us.mean())
+    achieved = alg_bytes / (fused_avg * 1e-6) / 1e9
+    value = alg_bytes / (step_us_wall * 1e-6) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_us_wall / 1e3, 4),
+        "us_per_step": round(step_us_wall, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 K/V + int4 K sketch (int8 x int4 scan, fp32 accumulate)",
+        "data": "synthetic (seeded; shapes and hot-block structure of the workload, no dataset)",
+        "config": {
+            "workload": w.name, "batch": w.B, "seq_len": (list(w.lens) if w.lens else list(w.len_range)),
+            "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "block_size": w.block_size,
+            "delta": None if dense else delta, "sink_blocks": w.sink, "local_blocks": w.local,
+            "split_blocks": w.split_blocks, "out_dtype": "f32",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "fused_decode_kernel (ffd_decode_partials)",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(w.name, delta, alg_bytes),
+            "algorithmic_bytes_per_launch": int(alg_bytes),
+            "avg_launch_us": round(fused_avg, 2),
+        },
+        "timing_us": {
+            "fused_median": round(float(np.median(fused_us)), 2),
+            "fused_p10": round(float(np.percentile(fused_us, 10)), 2),
+            "fused_p90": round(float(np.percentile(fused_us, 90)), 2),
+            "combine_median": round(float(np.median(comb_us)), 2),
+            "step_wall": round(step_us_wall, 2),
+            "quantize_build": round(quant_build_us, 1),
+        },
+        "bytes": {"scan": int(scan_b), "kv": int(kv_b)},
+        "kept_fraction": {"per_head": round(head_keep, 4), "gqa_union": round(union_keep, 4)},
+        "kernel_source_hash": kernel_source_hash(),
+        "input_gen_s": round(gen_s, 1),
+    }
+
+    if not args.no_dense and not dense:
+        wall_d, fused_d, _ = timed(math.inf, max(10, args.steps // 5), 3)
+        md = mask.cpu().numpy()
+        _, kv_d, _ = algorithmic_bytes(md, inp["seq_lens"], Hkv, G, d, w.block_size, True)
+        rec["dense_delta_inf"] = {
+            "us_per_step": round(wall_d / max(10, args.steps // 5) * 1e6, 2),
+            "fused_median_us": round(float(np.median(fused_d)), 2),
+            "fused_GBps": round(kv_d / (float(fused_d.mean()) * 1e-6) / 1e9, 1),
+            "sparse_speedup": round(float(np.median(fused_d)) / float(np.median(fused_us)), 3),
+        }
+
+    if not args.no_cpu_baseline:
+        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget)
+        smask = np.zeros_like(m)
+        for b, h in heads:
+            smask[b, h] = m[b, h]
+        # sample bytes: the (b, kv head) groups the sample covered, counted like the GPU step
+        sample_b = 0
+        groups = sorted({(b, h // G) for b, h in heads})
+        for b, j in groups:
+            sub = np.zeros((1, G, m.shape[2]), dtype=m.dtype)
+            sub[0] = m[b, j * G:(j + 1) * G]
+            s_scan, s_kv, _ = algorithmic_bytes(sub, inp["seq_lens"][b:b + 1], 1, G, d, w.block_size, dense)
+            sample_b += s_scan + s_kv
+        rec["cpu_baseline"] = {
+            "value": round(sample_b / t_cpu / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": (f"sequence 0, {len(groups)} of {w.B * w.Hkv} (sequence, kv head) groups "
+                       f"({len(heads)} query heads); NumPy oracle incl. its int4 key quantisation, "
+                       "single thread"),
+            "seconds": round(t_cpu, 2),
+            "us_per_step_extrapolated": round(t_cpu / len(groups) * (w.B * w.Hkv) * 1e6, 0),
+            "host_cpu": host_cpu_model(),
+            "host_cpu_count": os.cpu_count(),
+            "host_affinity": len(os.sched_getaffinity(0)),
+        }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

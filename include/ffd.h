@@ -60,7 +60,8 @@ const char* ffd_last_error(void);
  * (clamped to [0, cap)), with k = K[b, j, t, :]:
  *   amax = max_i |k_i|;  scale = fl32(amax / 7);  inv = fl32(7 / amax)
  *   code_i = clamp(round_half_even(fl32(k_i * inv)), -7, 7)
- *   (amax == 0: scale = 0 and every code 0)
+ *   (amax < 2^-125, zero included: scale = 0 and every code 0, since 7/amax
+ *   would overflow)
  * and stores kscale[b, j, t] = scale and the codes as two's-complement
  * nibbles, element 2i in the low nibble of byte i of kq[b, j, t, :].
  * Tokens outside the ranges are not touched.
@@ -97,8 +98,9 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  * L = clamp(seq_lens[b], 0, max_seq_len), NB = ceil(L / block_size). The
  * blocks of a sequence are cut into splits of `split_blocks` consecutive
  * blocks, one workgroup each. Per query head:
- *   1. The query is quantised to int8 (scale fl32(amax/127), codes
- *      clamp(rne(fl32(q_i * fl32(127/amax))), +-127)), cq = fl32(sq * sm_scale).
+ *   1. The query is quantised to int8 (scale sq = fl32(amax/127), codes
+ *      clamp(rne(fl32(q_i * fl32(127/amax))), +-127)), cq = fl32(sq * sm_scale);
+ *      amax < 2^-120 (zero included) gives all-zero codes and cq = 0.
  *   2. Scan ([TS] Methodology 3, "Top-δ Selection"): each valid token's
  *      tentative score is fl32(float(dot) * fl32(kscale_t * cq)), dot being
  *      the exact integer dot of the int8 query with the int4 codes; a block's
@@ -131,8 +133,11 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *   workspace  >= ffd_decode_workspace_bytes(B, Hq, d, max_seq_len,
  *              block_size, split_blocks) bytes, 256-byte aligned
  * A sequence with L == 0 gives out = 0, lse = -INFINITY and a zero mask row.
- * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8}.
- * q, k, v, kq must be 16-byte aligned.
+ * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8},
+ * at most 4096 splits per sequence (ceil(ceil(max_seq_len / 64) /
+ * split_blocks) <= 4096; FFD_ERR_UNSUPPORTED otherwise).
+ * q, k, v, kq must be 16-byte aligned. Equivalent to ffd_decode_partials
+ * followed by ffd_combine on the same stream.
  */
 ffd_status ffd_decode(const void* q, const void* k, const void* v,
                       const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
@@ -141,6 +146,43 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v,
                       int split_blocks, float sm_scale,
                       void* out, int out_dtype, float* lse, uint8_t* kept_mask,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ffd_decode_partials -- the first half of ffd_decode: the fused scan ->
+ * Top-δ select -> attend kernel, one workgroup per (sequence, kv head,
+ * split) ([TS] Methodology 3, "Fused Kernel"). Same arguments and semantics
+ * as ffd_decode (the kept_mask is written here); instead of the final output
+ * it leaves every split's partial result in the workspace:
+ *   n_splits = ceil(ceil(max_seq_len / block_size) / split_blocks)
+ *   o_part   f32 [B, Hq, n_splits, d] at byte offset 0: the split's
+ *            attention output, normalised over the split's kept tokens
+ *   lse_part f32 [B, Hq, n_splits] at byte offset
+ *            round_up(B*Hq*n_splits*d*4, 256): natural-log normaliser
+ * Only splits s < ceil(NB_b / split_blocks) of sequence b are written.
+ * Combining the partials of disjoint token sets by log-sum-exp is exact,
+ * which is what lets a sequence be split across workgroups (and, by the
+ * same merge, across devices) without any global maximum.
+ */
+ffd_status ffd_decode_partials(const void* q, const void* k, const void* v,
+                               const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
+                               int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
+                               int block_size, float delta, int sink_blocks, int local_blocks,
+                               int split_blocks, float sm_scale, uint8_t* kept_mask,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ffd_combine -- the second half of ffd_decode: per (sequence, query head),
+ *   lse = ln sum_s exp(lse_s),  out = sum_s exp(lse_s - lse) * o_s
+ * over the splits written by ffd_decode_partials (same seq_lens,
+ * max_seq_len, block_size and split_blocks; workspace laid out as described
+ * there). A sequence with L == 0 gives out = 0 and lse = -INFINITY.
+ * Supported: d in {64, 128}, block_size == 64, split_blocks in [1, 64],
+ * at most 4096 splits per sequence.
+ */
+ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, int d,
+                       int block_size, int split_blocks, const void* workspace,
+                       size_t workspace_bytes, void* out, int out_dtype, float* lse,
+                       void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,9 @@ from .ffd import (  # noqa: F401
     alloc_workspace,
     decode,
     ffd_abi_version,
+    ffd_combine,
     ffd_decode,
+    ffd_decode_partials,
     ffd_decode_workspace_bytes,
     ffd_last_error,
     ffd_quantize_kv,

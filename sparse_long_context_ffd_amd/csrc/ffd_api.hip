@@ -68,53 +68,61 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
   return ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns);
 }
 
-ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t* kq, const float* kscale,
-                      const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
-                      int block_size, float delta, int sink_blocks, int local_blocks, int split_blocks,
-                      float sm_scale, void* out, int out_dtype, float* lse, uint8_t* kept_mask, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || cap < 0 || max_seq_len < 0)
-    return fail(FFD_ERR_INVALID_ARG, "ffd_decode: bad sizes (B=%d Hq=%d Hkv=%d cap=%d max_seq_len=%d)", B, Hq, Hkv,
-                cap, max_seq_len);
-  if (Hq % Hkv) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: d must be positive and even (d=%d)", d);
-  if (cap < max_seq_len) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: cap=%d < max_seq_len=%d", cap, max_seq_len);
-  if (isnan(delta) || delta < 0.f) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: delta must be >= 0 (got %g)", (double)delta);
-  if (sink_blocks < 0 || local_blocks < 0)
-    return fail(FFD_ERR_INVALID_ARG, "ffd_decode: sink/local must be >= 0 (%d, %d)", sink_blocks, local_blocks);
-  if (split_blocks < 1) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: split_blocks must be >= 1 (got %d)", split_blocks);
-  if (!(sm_scale > 0.f) || isinf(sm_scale))
-    return fail(FFD_ERR_INVALID_ARG, "ffd_decode: sm_scale must be positive and finite (got %g)", (double)sm_scale);
-  if (out_dtype != FFD_OUT_BF16 && out_dtype != FFD_OUT_F32)
-    return fail(FFD_ERR_INVALID_ARG, "ffd_decode: unknown out_dtype %d", out_dtype);
-  if (block_size <= 0) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: block_size must be positive (got %d)", block_size);
-  const int G = Hq / Hkv;
-  if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "ffd_decode: d=%d not supported (64, 128)", d);
-  if (block_size != ffd::kBlockSize) return fail(FFD_ERR_UNSUPPORTED, "ffd_decode: block_size=%d not supported (64)", block_size);
-  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(FFD_ERR_UNSUPPORTED, "ffd_decode: group size %d not supported (1, 2, 4, 8)", G);
-  if (split_blocks > ffd::kMaxSplit)
-    return fail(FFD_ERR_UNSUPPORTED, "ffd_decode: split_blocks=%d not supported (<= %d)", split_blocks, ffd::kMaxSplit);
-  if (B == 0) return ok();
-  if (B > 65535 || Hkv > 65535 || Hq > 65535) return fail(FFD_ERR_UNSUPPORTED, "ffd_decode: B, Hq, Hkv must be <= 65535");
-  const bool dense = isinf(delta);
-  if (!q || !seq_lens || !out || !lse) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: null q/seq_lens/out/lse");
-  if (max_seq_len > 0 && (!k || !v)) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: null k/v");
-  if (max_seq_len > 0 && !dense && (!kq || !kscale))
-    return fail(FFD_ERR_INVALID_ARG, "ffd_decode: kq/kscale required unless delta is +inf");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kq))
-    return fail(FFD_ERR_INVALID_ARG, "ffd_decode: q, k, v, kq must be 16-byte aligned");
+}  // extern "C"
 
+namespace {
+
+// Validates the decode arguments shared by ffd_decode and ffd_decode_partials
+// and fills `p` (except the output fields). `need_bytes` gets the workspace
+// size the call requires.
+ffd_status prepare_decode(const char* fn, const void* q, const void* k, const void* v, const uint8_t* kq,
+                          const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv,
+                          int d, int cap, int block_size, float delta, int sink_blocks, int local_blocks,
+                          int split_blocks, float sm_scale, uint8_t* kept_mask, void* workspace,
+                          size_t workspace_bytes, ffd::DecodeParams& p, int& G, bool& dense) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || cap < 0 || max_seq_len < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: bad sizes (B=%d Hq=%d Hkv=%d cap=%d max_seq_len=%d)", fn, B, Hq, Hkv, cap,
+                max_seq_len);
+  if (Hq % Hkv) return fail(FFD_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
+  if (cap < max_seq_len) return fail(FFD_ERR_INVALID_ARG, "%s: cap=%d < max_seq_len=%d", fn, cap, max_seq_len);
+  if (isnan(delta) || delta < 0.f) return fail(FFD_ERR_INVALID_ARG, "%s: delta must be >= 0 (got %g)", fn, (double)delta);
+  if (sink_blocks < 0 || local_blocks < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: sink/local must be >= 0 (%d, %d)", fn, sink_blocks, local_blocks);
+  if (split_blocks < 1) return fail(FFD_ERR_INVALID_ARG, "%s: split_blocks must be >= 1 (got %d)", fn, split_blocks);
+  if (!(sm_scale > 0.f) || isinf(sm_scale))
+    return fail(FFD_ERR_INVALID_ARG, "%s: sm_scale must be positive and finite (got %g)", fn, (double)sm_scale);
+  if (block_size <= 0) return fail(FFD_ERR_INVALID_ARG, "%s: block_size must be positive (got %d)", fn, block_size);
+  G = Hq / Hkv;
+  if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
+  if (block_size != ffd::kBlockSize) return fail(FFD_ERR_UNSUPPORTED, "%s: block_size=%d not supported (64)", fn, block_size);
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(FFD_ERR_UNSUPPORTED, "%s: group size %d not supported (1, 2, 4, 8)", fn, G);
+  if (split_blocks > ffd::kMaxSplit)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: split_blocks=%d not supported (<= %d)", fn, split_blocks, ffd::kMaxSplit);
+  if (B > 65535 || Hkv > 65535 || Hq > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B, Hq, Hkv must be <= 65535", fn);
+  dense = isinf(delta);
+  if (B > 0) {
+    if (!q || !seq_lens) return fail(FFD_ERR_INVALID_ARG, "%s: null q/seq_lens", fn);
+    if (max_seq_len > 0 && (!k || !v)) return fail(FFD_ERR_INVALID_ARG, "%s: null k/v", fn);
+    if (max_seq_len > 0 && !dense && (!kq || !kscale))
+      return fail(FFD_ERR_INVALID_ARG, "%s: kq/kscale required unless delta is +inf", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kq))
+      return fail(FFD_ERR_INVALID_ARG, "%s: q, k, v, kq must be 16-byte aligned", fn);
+  }
   const int nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
-  const size_t need = max_seq_len > 0 ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
+  if (ns > ffd::kMaxSplits)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: %d splits per sequence exceed %d (raise split_blocks)", fn, ns,
+                ffd::kMaxSplits);
+  const size_t need = (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
   if (need > 0) {
-    if (!workspace) return fail(FFD_ERR_INVALID_ARG, "ffd_decode: null workspace");
+    if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);
     if (workspace_bytes < need)
-      return fail(FFD_ERR_WORKSPACE, "ffd_decode: workspace %zu bytes < required %zu", workspace_bytes, need);
+      return fail(FFD_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) % ffd::kWsAlign)
-      return fail(FFD_ERR_INVALID_ARG, "ffd_decode: workspace must be 256-byte aligned");
+      return fail(FFD_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   }
-  ffd::DecodeParams p{};
+  p = ffd::DecodeParams{};
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -125,9 +133,6 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
   p.o_part = need ? reinterpret_cast<float*>(ws) : nullptr;
   p.lse_part = need ? reinterpret_cast<float*>(ws + ffd::ws_opart_bytes(B, Hq, ns, d)) : nullptr;
   p.mask = kept_mask;
-  p.out = out;
-  p.lse = lse;
-  p.out_f32 = out_dtype == FFD_OUT_F32;
   p.max_seq_len = max_seq_len;
   p.B = B;
   p.Hq = Hq;
@@ -140,9 +145,116 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
   p.local = local_blocks;
   p.delta = delta;
   p.sm_scale = sm_scale;
-  hipError_t e = ffd::launch_decode(p, d, G, dense, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(FFD_ERR_HIP, "ffd_decode: launch failed: %s", hipGetErrorString(e));
+  return FFD_OK;
+}
+
+ffd_status check_out_dtype(const char* fn, int out_dtype) {
+  if (out_dtype != FFD_OUT_BF16 && out_dtype != FFD_OUT_F32)
+    return fail(FFD_ERR_INVALID_ARG, "%s: unknown out_dtype %d", fn, out_dtype);
+  return FFD_OK;
+}
+
+ffd_status check_out_ptrs(const char* fn, int B, void* out, float* lse) {
+  if (B > 0 && (!out || !lse)) return fail(FFD_ERR_INVALID_ARG, "%s: null out/lse", fn);
+  return FFD_OK;
+}
+
+ffd_status launch(const char* fn, const ffd::DecodeParams& p, int d, int G, bool dense, ffd::Stage stage,
+                  void* stream) {
+  if (p.B == 0) return ok();
+  hipError_t e = ffd::launch_decode(p, d, G, dense, stage, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FFD_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t* kq, const float* kscale,
+                      const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
+                      int block_size, float delta, int sink_blocks, int local_blocks, int split_blocks,
+                      float sm_scale, void* out, int out_dtype, float* lse, uint8_t* kept_mask, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  ffd::DecodeParams p;
+  int G;
+  bool dense;
+  ffd_status st = check_out_dtype("ffd_decode", out_dtype);
+  if (st != FFD_OK) return st;
+  st = prepare_decode("ffd_decode", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d, cap, block_size,
+                      delta, sink_blocks, local_blocks, split_blocks, sm_scale, kept_mask, workspace,
+                      workspace_bytes, p, G, dense);
+  if (st != FFD_OK) return st;
+  st = check_out_ptrs("ffd_decode", B, out, lse);
+  if (st != FFD_OK) return st;
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = out_dtype == FFD_OUT_F32;
+  return launch("ffd_decode", p, d, G, dense, ffd::Stage::kBoth, stream);
+}
+
+ffd_status ffd_decode_partials(const void* q, const void* k, const void* v, const uint8_t* kq,
+                               const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Hq,
+                               int Hkv, int d, int cap, int block_size, float delta, int sink_blocks,
+                               int local_blocks, int split_blocks, float sm_scale, uint8_t* kept_mask,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  ffd::DecodeParams p;
+  int G;
+  bool dense;
+  ffd_status st = prepare_decode("ffd_decode_partials", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d,
+                                 cap, block_size, delta, sink_blocks, local_blocks, split_blocks, sm_scale,
+                                 kept_mask, workspace, workspace_bytes, p, G, dense);
+  if (st != FFD_OK) return st;
+  return launch("ffd_decode_partials", p, d, G, dense, ffd::Stage::kPartials, stream);
+}
+
+ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, int d, int block_size,
+                       int split_blocks, const void* workspace, size_t workspace_bytes, void* out, int out_dtype,
+                       float* lse, void* stream) {
+  const char* fn = "ffd_combine";
+  if (B < 0 || Hq <= 0 || max_seq_len < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: bad sizes (B=%d Hq=%d max_seq_len=%d)", fn, B, Hq, max_seq_len);
+  if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
+  if (split_blocks < 1) return fail(FFD_ERR_INVALID_ARG, "%s: split_blocks must be >= 1 (got %d)", fn, split_blocks);
+  if (block_size <= 0) return fail(FFD_ERR_INVALID_ARG, "%s: block_size must be positive (got %d)", fn, block_size);
+  if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
+  if (block_size != ffd::kBlockSize) return fail(FFD_ERR_UNSUPPORTED, "%s: block_size=%d not supported (64)", fn, block_size);
+  if (split_blocks > ffd::kMaxSplit)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: split_blocks=%d not supported (<= %d)", fn, split_blocks, ffd::kMaxSplit);
+  if (B > 65535 || Hq > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B, Hq must be <= 65535", fn);
+  ffd_status st = check_out_dtype(fn, out_dtype);
+  if (st != FFD_OK) return st;
+  st = check_out_ptrs(fn, B, out, lse);
+  if (st != FFD_OK) return st;
+  if (B > 0 && !seq_lens) return fail(FFD_ERR_INVALID_ARG, "%s: null seq_lens", fn);
+  const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
+  if (ns > ffd::kMaxSplits)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: %d splits per sequence exceed %d (raise split_blocks)", fn, ns,
+                ffd::kMaxSplits);
+  const size_t need = (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
+  if (need > 0) {
+    if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);
+    if (workspace_bytes < need)
+      return fail(FFD_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) % ffd::kWsAlign)
+      return fail(FFD_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  }
+  ffd::DecodeParams p{};
+  const char* ws = static_cast<const char*>(workspace);
+  p.o_part = need ? reinterpret_cast<float*>(const_cast<char*>(ws)) : nullptr;
+  p.lse_part = need ? reinterpret_cast<float*>(const_cast<char*>(ws) + ffd::ws_opart_bytes(B, Hq, ns, d)) : nullptr;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = out_dtype == FFD_OUT_F32;
+  p.max_seq_len = max_seq_len;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = 1;
+  p.nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
+  p.n_splits = ns;
+  p.split_blocks = split_blocks;
+  return launch(fn, p, d, 1, false, ffd::Stage::kCombine, stream);
 }
 
 }  // extern "C"

@@ -23,13 +23,21 @@
 //            sink/local blocks, mask store, and a ballot-compacted list of the
 //            blocks kept by at least one head of the group (with a per-head
 //            bit mask).
-//  attend    waves take kept blocks round-robin; D/8 lanes own one token row
-//            (16 B of K and of V each). The running max of every head starts
-//            at the scan's split max (the scan result reused to seed the
-//            softmax), so rescaling is rare; a head skips the blocks it did
-//            not keep.
-//  epilogue  wave and token-group partials merged in registers/LDS; the
-//            split's normalised output and natural-log LSE go to workspace.
+//  attend    waves take kept blocks round-robin, one 64-token block at a
+//            time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the G query
+//            heads padded to 16 columns):
+//              QK  A = K rows straight from HBM into registers (16 tokens x
+//                  32 dims per MFMA; each lane reads D/2 contiguous bytes of a
+//                  row), B = the bf16 query, 4*(D/32) MFMAs per block;
+//              softmax in the MFMA output layout (lane = head, 4 tokens per
+//                  tile); the running max of every head starts at the scan's
+//                  split max (the scan result reused to seed the softmax) so
+//                  rescaling is rare; heads skip blocks they did not keep;
+//              PV  A = P as bf16 hi + lo parts (~fp32 precision), B = V, staged
+//                  through a per-wave XOR-swizzled LDS tile and read with the
+//                  transposing ds_read_b64_tr_b16, 2*2*(D/16) MFMAs per block.
+//  epilogue  wave partials merged through LDS; the split's normalised output
+//            and natural-log LSE go to workspace.
 #include <math.h>
 
 #include "ffd_device.h"
@@ -44,7 +52,8 @@ constexpr int kWaves = kThreads / kWave;
 
 template <int D, int G>
 struct DecodeSmem {
-  float q[G][D];            // bf16 query, fp32, times sm_scale * log2(e)
+  uint16_t vt[kWaves][kBlockSize * D];  // per-wave V tile (bf16, swizzled rows)
+  float q[G][D];            // bf16 query widened to fp32 (prologue only)
   int8_t qc[G][D];          // int8 scan query
   float cq[G];              // fl32(sq * sm_scale)
   int sumq[G];              // sum of qc (offset-binary correction)
@@ -57,6 +66,11 @@ struct DecodeSmem {
   float wl[kWaves][G];
   float wo[kWaves][G][D];
 };
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) {
   return (int)((uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
@@ -94,71 +108,79 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
   const uint8_t* kq = p.kq + bh * (size_t)p.cap * (D / 2);
   const float* ks = p.kscale + bh * (size_t)p.cap;
 
-  for (int jl = w; jl < nblk; jl += kWaves) {
-    const int t0 = (j0 + jl) * kBlockSize;
-    uint32_t cw[4][NCW];
-    float sc[4];
-    bool valid[4];
+  // Each wave owns blocks w, w+4, w+8, ...; kChunk of them are loaded at once
+  // (kChunk*4 KiB of codes in flight per wave) before any is reduced.
+  constexpr int kChunk = 4;
+  for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
+    u32x4_t cw[kChunk][4];
+    float sc[kChunk][4];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int t = t0 + it * 16 + quad;
-      valid[it] = t < L;
-      if (valid[it]) {
-        const uint8_t* src = kq + (size_t)t * (D / 2) + ql * (D / 8);
-        if constexpr (NCW == 4) {
-          uint4 u = *reinterpret_cast<const uint4*>(src);
-          cw[it][0] = u.x; cw[it][1] = u.y; cw[it][2] = u.z; cw[it][3] = u.w;
-        } else {
-          uint2 u = *reinterpret_cast<const uint2*>(src);
-          cw[it][0] = u.x; cw[it][1] = u.y;
+    for (int c = 0; c < kChunk; ++c) {
+      const int jl = jc + c * kWaves;
+      if (jl < nblk) {
+        const int t0 = (j0 + jl) * kBlockSize;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int t = t0 + it * 16 + quad;
+          const bool ok = t < L;
+          const uint8_t* src = kq + (size_t)(ok ? t : 0) * (D / 2) + ql * (D / 8);
+          if constexpr (NCW == 4) {
+            cw[c][it] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+          } else {
+            const uint2 u = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+            cw[c][it] = u32x4_t{u.x, u.y, 0u, 0u};
+          }
+          sc[c][it] = ok ? ks[t] : 0.f;
         }
-        sc[it] = ks[t];
-      } else {
-#pragma unroll
-        for (int i = 0; i < NCW; ++i) cw[it][i] = 0u;
-        sc[it] = 0.f;
       }
     }
-    float bm[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
+    for (int c = 0; c < kChunk; ++c) {
+      const int jl = jc + c * kWaves;
+      if (jl >= nblk) continue;
+      const int t0 = (j0 + jl) * kBlockSize;
+      float bm[G];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      int acc[G];
+      for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = 0;
+      for (int it = 0; it < 4; ++it) {
+        int acc[G];
 #pragma unroll
-      for (int i = 0; i < NCW; ++i) {
-        const uint32_t x = cw[it][i] ^ 0x88888888u;   // two's complement -> code + 8
-        const int lo = (int)(x & 0x0f0f0f0fu);
-        const int hi = (int)((x >> 4) & 0x0f0f0f0fu);
+        for (int h = 0; h < G; ++h) acc[h] = 0;
+#pragma unroll
+        for (int i = 0; i < NCW; ++i) {
+          const uint32_t x = cw[c][it][i] ^ 0x88888888u;   // two's complement -> code + 8
+          const int lo = (int)(x & 0x0f0f0f0fu);
+          const int hi = (int)((x >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h] = __builtin_amdgcn_sdot4(lo, qe[h][i], acc[h], false);
+            acc[h] = __builtin_amdgcn_sdot4(hi, qo[h][i], acc[h], false);
+          }
+        }
+        const bool ok = t0 + it * 16 + quad < L;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          acc[h] = __builtin_amdgcn_sdot4(lo, qe[h][i], acc[h], false);
-          acc[h] = __builtin_amdgcn_sdot4(hi, qo[h][i], acc[h], false);
+          const int dot = quad_sum_i(acc[h]) - corr[h];
+          const float wgt = sc[c][it] * cq[h];
+          const float sv = (float)dot * wgt;
+          if (ok) bm[h] = fmaxf(bm[h], sv);
         }
       }
+      // max over the 16 quads (each quad's lanes hold identical values)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const int dot = quad_sum_i(acc[h]) - corr[h];
-        const float wgt = sc[it] * cq[h];
-        const float s = (float)dot * wgt;
-        if (valid[it]) bm[h] = fmaxf(bm[h], s);
+        float m = bm[h];
+        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+        m = fmaxf(m, dpp_f<kDppMirror>(m));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        bm[h] = m;
       }
-    }
-    // max over the 16 quads (each quad's lanes hold identical values)
+      if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float m = bm[h];
-      m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
-      m = fmaxf(m, dpp_f<kDppMirror>(m));
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      bm[h] = m;
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) sm.blk[jl][h] = bm[h];
+        for (int h = 0; h < G; ++h) sm.blk[jl][h] = bm[h];
+      }
     }
   }
 }
@@ -205,77 +227,184 @@ __device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<
 
 // ---------------------------------------------------------------------------
 // attend: exact attention over the kept blocks ([TS] Methodology 3,
-// "Fine-Grained Refinement"), VALU version.
+// "Fine-Grained Refinement") on the matrix cores.
 // ---------------------------------------------------------------------------
-template <int D, int G, bool DENSE>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, size_t bh, int j0,
-                                              int L, int lane, int w, float (&m)[G], float (&l)[G],
-                                              float (&o)[G][8]) {
-  constexpr int LPT = D / 8;      // lanes per token row
-  constexpr int TPI = kWave / LPT;  // token rows per wave load
-  const int tg = lane / LPT;
-  const int c = lane % LPT;
-  float qr[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qr[h][e] = sm.q[h][c * 8 + e];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = DENSE ? -INFINITY : sm.seed[h] * kLog2e;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  }
-  const uint16_t* kb = p.k + bh * (size_t)p.cap * D;
-  const uint16_t* vb = p.v + bh * (size_t)p.cap * D;
-  const int nkept = sm.nkept;
-  for (int e = w; e < nkept; e += kWaves) {
-    const int jb = j0 + sm.kidx[e];
-    const unsigned hm = sm.khm[e];
-    for (int it = 0; it < kBlockSize / TPI; ++it) {
-      const int t = jb * kBlockSize + it * TPI + tg;
-      const bool valid = t < L;
-      uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
-      if (valid) {
-        kw = *reinterpret_cast<const uint4*>(kb + (size_t)t * D + c * 8);
-        vw = *reinterpret_cast<const uint4*>(vb + (size_t)t * D + c * 8);
-      }
-      const float kf[8] = {bf16_lo(kw.x), bf16_hi(kw.x), bf16_lo(kw.y), bf16_hi(kw.y),
-                           bf16_lo(kw.z), bf16_hi(kw.z), bf16_lo(kw.w), bf16_hi(kw.w)};
-      const float vf[8] = {bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y),
-                           bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)};
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s += qr[h][i] * kf[i];
-        s = group_sum_f<LPT>(s);
-        if (!valid || !((hm >> h) & 1u)) s = -INFINITY;
-        if (s > m[h]) {
-          const float a = exp2f(m[h] - s);
-          l[h] *= a;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[h][i] *= a;
-          m[h] = s;
-        }
-        const float pr = (s == -INFINITY) ? 0.f : exp2f(s - m[h]);
-        l[h] += pr;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[h][i] += pr * vf[i];
-      }
-    }
+
+// LDS byte offset of 16-byte chunk `q` of V row `r` in a wave's tile. Rows are
+// 2*D bytes; pairs of chunks are XOR-swizzled by row so that the 16 rows x
+// 32 bytes one transposing read touches fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int vt_off(int r, int q) {
+  if constexpr (D == 128) {
+    return r * 256 + ((q ^ ((r & 7) << 1)) << 4);
+  } else {
+    return r * 128 + ((q ^ (((r >> 1) & 3) << 1)) << 4);
   }
 }
 
-// Merge two online-softmax states (base-2 logits).
-__device__ __forceinline__ void merge_state(float& m, float& l, float* o, int n, float m2, float l2, const float* o2) {
-  const float mn = fmaxf(m, m2);
-  const float a = (m == -INFINITY) ? 0.f : exp2f(m - mn);
-  const float b = (m2 == -INFINITY) ? 0.f : exp2f(m2 - mn);
-  l = l * a + l2 * b;
-  for (int i = 0; i < n; ++i) o[i] = o[i] * a + o2[i] * b;
-  m = mn;
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each aligned group of 16
+// lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
+// i/4, 4+i/4, 8+i/4 and 12+i/4 of its group.
+__device__ __forceinline__ bf16x4_t lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      reinterpret_cast<bf16x4_t __attribute__((address_space(3)))*>((__attribute__((address_space(3))) char*)p));
+}
+
+// Per-wave online-softmax state of the attend phase. Lane l serves query head
+// h = l % 16 (rows h >= G are padding) for the tokens 4*(l/16)..+3 of every
+// 16-token tile; o[nt][r] holds output row 4*(l/16)+r, column 16*nt + l%16.
+template <int D>
+struct AttendState {
+  f32x4_t o[D / 16];
+  float m;   // running max (base-2 logits), same in the 4 lanes of a head
+  float l;   // this lane's share of the normaliser
+};
+
+template <int D, int G, bool DENSE>
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, size_t bh, int b,
+                                              int j, int j0, int L, int lane, int w, AttendState<D>& st) {
+  constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
+  constexpr int NT = D / 16;    // MFMA n-tiles of the output
+  constexpr int VC = D / 8;     // 16-byte chunks per V row
+  constexpr int VL = 64 * VC / kWave;  // 16-byte V loads per lane per block
+  const int h = lane & 15;
+  const int g = lane >> 4;
+
+  // B operand of QK: the bf16 query of head h, dims g*D/4 + 8s .. +8 for k-step s
+  bf16x8_t qop[KS];
+  {
+    const uint16_t* qh = p.q + ((size_t)b * p.Hq + (size_t)j * G + (h < G ? h : 0)) * D + g * (D / 4);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4_t u = u32x4_t{0u, 0u, 0u, 0u};
+      if (h < G) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
+      qop[s] = as_bf16x8(u);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) st.o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  st.m = (h < G) ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
+  st.l = 0.f;
+
+  const uint16_t* kb = p.k + bh * (size_t)p.cap * D;
+  const uint16_t* vb = p.v + bh * (size_t)p.cap * D;
+  char* vt = reinterpret_cast<char*>(sm.vt[w]);
+  // LDS addresses of the V tile. Store: 16-byte chunk n*64 + lane of the tile
+  // goes to wbase[n & 1] + (n >> 1) * 2048 (the row swizzle repeats every 8
+  // rows for D=128, and every 2 stores for D=64). Transposed read for k-step
+  // ks, half hf, n-tile nt: rbase + 32 rows*ks + 16 rows*hf + ((nt ^ rx) << 5).
+  constexpr int ROWB = 2 * D;
+  constexpr int RPS = kWave / VC;   // rows per 1 KiB store
+  int wbase[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) wbase[par] = vt_off<D>(par * RPS + lane / VC, lane % VC);
+  const int rr = 4 * g + (h >> 2);
+  const int rx = (D == 128) ? (rr & 7) : ((rr >> 1) & 3);
+  const int rbase = rr * ROWB + ((h & 3) >> 1) * 16 + (h & 1) * 8;
+  const float zscale = p.sm_scale * kLog2e;
+  const int nkept = sm.nkept;
+
+  for (int e = w; e < nkept; e += kWaves) {
+    const int jb = j0 + sm.kidx[e];
+    const unsigned hm = sm.khm[e];
+    const int t0 = jb * kBlockSize;
+    const int tlast = L - 1;   // rows past the sequence are read from its last row and masked
+
+    // ---- issue the block's loads: K into registers, V into registers ----
+    u32x4_t kr[4][KS];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int t = min(t0 + 16 * T + h, tlast);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)t * D + g * (D / 4));
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kr[T][s] = src[s];
+    }
+    u32x4_t vr[VL];
+#pragma unroll
+    for (int n = 0; n < VL; ++n) {
+      const int f = n * kWave + lane;        // chunk id within the tile
+      const int r = f / VC, q = f % VC;
+      const int t = min(t0 + r, tlast);
+      vr[n] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)t * D + q * 8);
+    }
+
+    // ---- QK on the matrix cores ----
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      sacc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[T][s]), qop[s], sacc[T], 0, 0, 0);
+    }
+
+    // ---- V tile to LDS (this wave's region) ----
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int n = 0; n < VL; ++n)
+      *reinterpret_cast<u32x4_t*>(vt + wbase[n & 1] + (n >> 1) * 2048) = vr[n];
+
+    // ---- online softmax in the MFMA output layout ----
+    const bool head_keeps = (h < G) && ((hm >> h) & 1u);
+    float sv[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 16 * T + 4 * g + r;
+        const float z = sacc[T][r] * zscale;
+        sv[T][r] = (head_keeps && t < L) ? z : -INFINITY;
+        mx = fmaxf(mx, sv[T][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool up = mx > st.m;
+    if (__ballot(up)) {
+      const float mn = up ? mx : st.m;
+      const float alpha = (st.m == -INFINITY) ? 0.f : exp2f(st.m - mn);
+      st.m = mn;
+      st.l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.o[nt][r] *= ar;
+      }
+    }
+    bf16x8_t phi[2], plo[2];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = (sv[T][r] == -INFINITY) ? 0.f : exp2f(sv[T][r] - st.m);
+        st.l += pr;
+        const __bf16 hi = (__bf16)pr;
+        const __bf16 lo = (__bf16)(pr - (float)hi);
+        phi[T >> 1][(T & 1) * 4 + r] = hi;
+        plo[T >> 1][(T & 1) * 4 + r] = lo;
+      }
+
+    // ---- PV on the matrix cores: B = V read transposed from LDS ----
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        // providing lane (g, h): row 32ks + 16hf + 4g + h/4, dims 16nt + 4(h%4) .. +4
+        const char* a = vt + rbase + ks * 32 * ROWB + ((nt ^ rx) << 5);
+        const bf16x4_t v0 = lds_read_tr(a);
+        const bf16x4_t v1 = lds_read_tr(a + 16 * ROWB);
+        const bf16x8_t vb8 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[ks], vb8, st.o[nt], 0, 0, 0);
+        st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb8, st.o[nt], 0, 0, 0);
+      }
+    }
+  }
 }
 
 template <int D, int G, bool DENSE>
@@ -353,34 +482,26 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   __syncthreads();
 
   // ---- attend -------------------------------------------------------------
-  float m[G], l[G], o[G][8];
-  attend_blocks<D, G, DENSE>(p, sm, bh, j0, L, lane, w, m, l, o);
+  AttendState<D> st;
+  attend_blocks<D, G, DENSE>(p, sm, bh, b, j, j0, L, lane, w, st);
 
-  // merge the token groups of this wave (lanes that differ by multiples of D/8)
-  constexpr int LPT = D / 8;
+  // this wave's partial: normaliser of head h summed over its 4 lane groups
+  float lw = st.l;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  {
+    const int g = lane >> 4;
 #pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 4 * g + r;
+      if (hh < G) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m2 = __shfl_xor(m[h], off);
-      const float l2 = __shfl_xor(l[h], off);
-      float o2[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(o[h][i], off);
-      merge_state(m[h], l[h], o[h], 8, m2, l2, o2);
+        for (int nt = 0; nt < D / 16; ++nt) sm.wo[w][hh][16 * nt + (lane & 15)] = st.o[nt][r];
+      }
     }
-  }
-  if (lane < LPT) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.wo[w][h][lane * 8 + i] = o[h][i];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sm.wm[w][h] = m[h];
-      sm.wl[w][h] = l[h];
+    if (lane < G) {
+      sm.wm[w][lane] = st.m;
+      sm.wl[w][lane] = lw;
     }
   }
   __syncthreads();
@@ -408,8 +529,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 // split combine: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(const DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(256) void combine_kernel(const DecodeParams p) {
+  constexpr int PARTS = 256 / D;   // split subsets summed in parallel
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[PARTS][D];
+  __shared__ float s_lse;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
   const int NB = (L + kBlockSize - 1) / kBlockSize;
@@ -417,53 +542,71 @@ __global__ __launch_bounds__(D) void combine_kernel(const DecodeParams p) {
   const size_t bh = (size_t)b * p.Hq + h;
   const float* lp = p.lse_part + bh * p.n_splits;
   const float* op = p.o_part + bh * p.n_splits * D;
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lp[s]);
-  float den = 0.f, num = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float a = (lp[s] == -INFINITY) ? 0.f : expf(lp[s] - mx);
-    den += a;
-    num += a * op[(size_t)s * D + c];
+  // weights exp(lse_s - lse) of the splits, computed by wave 0
+  if (tid < kWave) {
+    float mx = -INFINITY;
+    for (int s = tid; s < ns; s += kWave) mx = fmaxf(mx, lp[s]);
+    mx = wave_max_f(mx);
+    float den = 0.f;
+    for (int s = tid; s < ns; s += kWave) den += (lp[s] == -INFINITY) ? 0.f : expf(lp[s] - mx);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+    const float lse = (ns > 0 && den > 0.f) ? mx + logf(den) : -INFINITY;
+    for (int s = tid; s < ns; s += kWave) wgt[s] = (lse == -INFINITY) ? 0.f : expf(lp[s] - lse);
+    if (tid == 0) s_lse = lse;
   }
-  float res = 0.f, lse = -INFINITY;
-  if (ns > 0 && den > 0.f) {
-    res = num / den;
-    lse = mx + logf(den);
+  __syncthreads();
+  const int c = tid % D, part = tid / D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = part;
+  for (; s + 3 * PARTS < ns; s += 4 * PARTS) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += wgt[s + u * PARTS] * op[(size_t)(s + u * PARTS) * D + c];
   }
-  if (p.out_f32) {
-    static_cast<float*>(p.out)[bh * D + c] = res;
-  } else {
-    static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16(res);
+  for (; s < ns; s += PARTS) acc[0] += wgt[s] * op[(size_t)s * D + c];
+  red[part][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (part == 0) {
+    float res = 0.f;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) res += red[q][c];
+    if (p.out_f32) {
+      static_cast<float*>(p.out)[bh * D + c] = res;
+    } else {
+      static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16(res);
+    }
+    if (c == 0) p.lse[bh] = s_lse;
   }
-  if (c == 0) p.lse[bh] = lse;
 }
 
 template <int D, int G, bool DENSE>
-hipError_t launch_fused(const DecodeParams& p, hipStream_t stream) {
-  if (p.n_splits > 0) {
+hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) {
+  if ((static_cast<int>(stage) & static_cast<int>(Stage::kPartials)) && p.n_splits > 0) {
     dim3 grid(p.n_splits, p.Hkv, p.B);
     fused_decode_kernel<D, G, DENSE><<<grid, kThreads, 0, stream>>>(p);
   }
-  combine_kernel<D><<<dim3(p.Hq, p.B), D, 0, stream>>>(p);
+  if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
+    combine_kernel<D><<<dim3(p.Hq, p.B), 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
 template <int D, bool DENSE>
-hipError_t launch_g(const DecodeParams& p, int G, hipStream_t stream) {
+hipError_t launch_g(const DecodeParams& p, int G, Stage stage, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_fused<D, 1, DENSE>(p, stream);
-    case 2: return launch_fused<D, 2, DENSE>(p, stream);
-    case 4: return launch_fused<D, 4, DENSE>(p, stream);
-    case 8: return launch_fused<D, 8, DENSE>(p, stream);
+    case 1: return launch_fused<D, 1, DENSE>(p, stage, stream);
+    case 2: return launch_fused<D, 2, DENSE>(p, stage, stream);
+    case 4: return launch_fused<D, 4, DENSE>(p, stage, stream);
+    case 8: return launch_fused<D, 8, DENSE>(p, stage, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, hipStream_t stream) {
-  if (D == 128) return dense ? launch_g<128, true>(p, G, stream) : launch_g<128, false>(p, G, stream);
-  if (D == 64) return dense ? launch_g<64, true>(p, G, stream) : launch_g<64, false>(p, G, stream);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream) {
+  if (D == 128) return dense ? launch_g<128, true>(p, G, stage, stream) : launch_g<128, false>(p, G, stage, stream);
+  if (D == 64) return dense ? launch_g<64, true>(p, G, stage, stream) : launch_g<64, false>(p, G, stage, stream);
   return hipErrorInvalidValue;
 }
 

@@ -9,6 +9,7 @@ namespace ffd {
 
 constexpr int kBlockSize = 64;   // tokens per selection block
 constexpr int kMaxSplit = 64;    // max blocks per split (one workgroup)
+constexpr int kMaxSplits = 4096; // max splits per sequence (combine keeps their weights in LDS)
 constexpr size_t kWsAlign = 256;
 
 struct DecodeParams {
@@ -45,7 +46,9 @@ hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, con
                               const int32_t* pos_end, int B, int Hkv, int cap, int D, int max_span,
                               hipStream_t stream);
 
+enum class Stage { kPartials = 1, kCombine = 2, kBoth = 3 };
+
 // Returns hipErrorInvalidValue for an unsupported (D, G) pair.
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream);
 
 }  // namespace ffd

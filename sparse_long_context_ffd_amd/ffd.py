@@ -6,6 +6,7 @@ memory and the current HIP stream. If the library has not been built this
 module raises on first use; there is no fallback.
 
 Low-level entry points keep the C names (``ffd_quantize_kv``, ``ffd_decode``,
+``ffd_decode_partials``, ``ffd_combine``,
 ``ffd_decode_workspace_bytes``, ``ffd_last_error``, ``ffd_abi_version``) and
 take preallocated tensors. ``quantize_kv`` and ``decode`` are conveniences
 that allocate the outputs and the workspace with torch and then call them.
@@ -31,7 +32,7 @@ FFD_OUT_BF16 = 0
 FFD_OUT_F32 = 1
 
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_decode_workspace_bytes",
-                    "ffd_decode")
+                    "ffd_decode", "ffd_decode_partials", "ffd_combine")
 
 
 class FFDError(RuntimeError):
@@ -70,6 +71,12 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_float,                        # sm_scale
                              _vp, _i, _vp, _vp,                     # out out_dtype lse mask
                              _vp, ctypes.c_size_t, _vp]             # workspace bytes stream
+    L.ffd_decode_partials.restype = _i
+    L.ffd_decode_partials.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                      _i, ctypes.c_float, _i, _i, _i, ctypes.c_float,
+                                      _vp, _vp, ctypes.c_size_t, _vp]
+    L.ffd_combine.restype = _i
+    L.ffd_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _i, _vp, _vp]
     _lib = L
     return L
 
@@ -125,12 +132,7 @@ def ffd_quantize_kv(k: torch.Tensor, kq: torch.Tensor, kscale: torch.Tensor, pos
                                  B, Hkv, cap, d, int(max_span), _stream(stream)))
 
 
-def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[torch.Tensor],
-               kscale: Optional[torch.Tensor], seq_lens: torch.Tensor, *, max_seq_len: int, block_size: int,
-               delta: float, sink: int, local: int, split_blocks: int, sm_scale: float, out: torch.Tensor,
-               lse: torch.Tensor, kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
-               stream=None) -> None:
-    """One decode step into preallocated ``out`` / ``lse`` / ``kept_mask``."""
+def _check_decode_inputs(q, k, v, kq, kscale, seq_lens, max_seq_len, block_size, kept_mask):
     _need(q, "q", torch.bfloat16, 3)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -139,27 +141,67 @@ def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[t
     if tuple(k.shape) != (B, Hkv, cap, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError("k/v shapes do not match q")
     _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens needs one entry per sequence")
     if kq is not None:
         _need(kq, "kq", torch.uint8, 4)
         _need(kscale, "kscale", torch.float32, 3)
         if tuple(kq.shape) != (B, Hkv, cap, d // 2) or tuple(kscale.shape) != (B, Hkv, cap):
             raise ValueError("kq/kscale shapes do not match k")
+    if kept_mask is not None:
+        _need(kept_mask, "kept_mask", torch.uint8, 3)
+        if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
+            raise ValueError("kept_mask shape")
+    return B, Hq, Hkv, d, cap
+
+
+def _check_outputs(out, lse, B, Hq, d):
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("out must be bf16 or f32")
     _need(out, "out", out.dtype, 3)
     _need(lse, "lse", torch.float32, 2)
     if tuple(out.shape) != (B, Hq, d) or tuple(lse.shape) != (B, Hq):
         raise ValueError("out/lse shapes")
-    if kept_mask is not None:
-        _need(kept_mask, "kept_mask", torch.uint8, 3)
-        if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
-            raise ValueError("kept_mask shape")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return FFD_OUT_F32 if out.dtype == torch.float32 else FFD_OUT_BF16
+
+
+def _ws(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[torch.Tensor],
+               kscale: Optional[torch.Tensor], seq_lens: torch.Tensor, *, max_seq_len: int, block_size: int,
+               delta: float, sink: int, local: int, split_blocks: int, sm_scale: float, out: torch.Tensor,
+               lse: torch.Tensor, kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
+               stream=None) -> None:
+    """One decode step into preallocated ``out`` / ``lse`` / ``kept_mask``."""
+    B, Hq, Hkv, d, cap = _check_decode_inputs(q, k, v, kq, kscale, seq_lens, max_seq_len, block_size, kept_mask)
+    odt = _check_outputs(out, lse, B, Hq, d)
     _check(lib().ffd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
                             int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta), int(sink),
-                            int(local), int(split_blocks), float(sm_scale), _ptr(out),
-                            FFD_OUT_F32 if out.dtype == torch.float32 else FFD_OUT_BF16, _ptr(lse),
-                            _ptr(kept_mask), _ptr(workspace), ws_bytes, _stream(stream)))
+                            int(local), int(split_blocks), float(sm_scale), _ptr(out), odt, _ptr(lse),
+                            _ptr(kept_mask), _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def ffd_decode_partials(q, k, v, kq, kscale, seq_lens, *, max_seq_len: int, block_size: int, delta: float,
+                        sink: int, local: int, split_blocks: int, sm_scale: float,
+                        kept_mask: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+    """The fused scan -> select -> attend kernel alone; partials stay in ``workspace``."""
+    B, Hq, Hkv, d, cap = _check_decode_inputs(q, k, v, kq, kscale, seq_lens, max_seq_len, block_size, kept_mask)
+    _check(lib().ffd_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
+                                     int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta),
+                                     int(sink), int(local), int(split_blocks), float(sm_scale), _ptr(kept_mask),
+                                     _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def ffd_combine(seq_lens, *, max_seq_len: int, block_size: int, split_blocks: int, workspace: torch.Tensor,
+                out: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
+    """Log-sum-exp merge of the per-split partials in ``workspace`` into ``out`` / ``lse``."""
+    B, Hq, d = out.shape
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    odt = _check_outputs(out, lse, B, Hq, d)
+    _check(lib().ffd_combine(_ptr(seq_lens), int(max_seq_len), B, Hq, d, int(block_size), int(split_blocks),
+                             _ptr(workspace), _ws(workspace), _ptr(out), odt, _ptr(lse), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -24,7 +24,8 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = ffd.lib()
     names = _declared()
-    assert set(names) >= {"ffd_quantize_kv", "ffd_decode", "ffd_decode_workspace_bytes"}
+    assert set(names) >= {"ffd_quantize_kv", "ffd_decode", "ffd_decode_workspace_bytes", "ffd_decode_partials",
+                          "ffd_combine"}
     for n in names:
         assert hasattr(L, n), n
     dyn = subprocess.run(["nm", "-D", "--defined-only", ffd.LIB_PATH], capture_output=True, text=True).stdout

@@ -28,7 +28,7 @@ CASES = [
     (2, 16, 2, 64, (3000, 2999), INF, 1, 4, 32, {}),
     (1, 8, 2, 128, (300,), 0.0, 3, 3, 2, {}),
     (1, 4, 2, 128, (5000,), 3.0, 1, 2, 5, {"max_seq_len": 3000}),
-    (2, 8, 2, 128, (700, 1500), 1.5, 1, 1, 7, {"out_dtype": torch.float32}),
+    (2, 8, 2, 128, (700, 1500), 1.5, 1, 1, 7, {"out_dtype": torch.bfloat16}),
     (1, 2, 1, 64, (4097,), 0.25, 0, 1, 64, {}),
     (1, 4, 4, 128, (64 * 64 + 1,), 4.0, 1, 1, 64, {}),
 ]
@@ -42,14 +42,36 @@ def test_small_cases(case):
     msl = extra.get("max_seq_len", inp["cap"])
     sm = sm_scale_for(d)
     dv = to_device(inp)
+    out_dtype = extra.get("out_dtype", torch.float32)
     out, lse, mask = run_gpu(dv, max_seq_len=msl, delta=delta, sink=sink, local=local, split_blocks=S,
-                             sm_scale=sm, out_dtype=extra.get("out_dtype", torch.bfloat16))
+                             sm_scale=sm, out_dtype=out_dtype)
     r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=msl,
                                     block_size=64, delta=delta, sink=sink, local=local, split_blocks=S,
                                     sm_scale=np.float32(sm))
     assert_mask_equal(mask, r_mask, "mask")
-    assert_close(out, r_out, "out")
+    assert_close(out, r_out, "out", bf16_out=out_dtype == torch.bfloat16)
     assert_close(lse, r_lse, "lse")
+
+
+@pytest.mark.parametrize("case", [0, 3, 4, 6])
+def test_bf16_output(case):
+    """bf16 output = the fp32 result rounded half to even: within the bar plus
+    half a bf16 ulp of the reference, and equal to rounding the fp32 output."""
+    B, Hq, Hkv, d, lens, delta, sink, local, S, extra = CASES[case]
+    say(f"decode bf16 output case {case}")
+    inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=100 + case, block_size=64, hot_frac=0.05)
+    msl = extra.get("max_seq_len", inp["cap"])
+    dv = to_device(inp)
+    kw = dict(max_seq_len=msl, delta=delta, sink=sink, local=local, split_blocks=S, sm_scale=sm_scale_for(d))
+    out16, lse16, mask16 = run_gpu(dv, out_dtype=torch.bfloat16, **kw)
+    out32, lse32, mask32 = run_gpu(dv, out_dtype=torch.float32, **kw)
+    np.testing.assert_array_equal(mask16, mask32)
+    np.testing.assert_array_equal(lse16, lse32)
+    rounded = torch.from_numpy(out32.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(out16, rounded)
+    r_out, _, _ = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], block_size=64,
+                           sm_scale=np.float32(kw.pop("sm_scale")), **kw)
+    assert_close(out16, r_out, "bf16 out", bf16_out=True)
 
 
 def test_tiny_workload_and_dense_limit():
@@ -121,3 +143,25 @@ def test_no_mask_pointer_and_reused_workspace():
         ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], delta=1.0, split_blocks=16,
                    workspace=ws[:100])
     assert ei.value.status == ffd.FFD_ERR_WORKSPACE
+
+
+def test_partials_then_combine_equals_decode():
+    say("decode = partials + combine")
+    inp = make_random_inputs(3, 16, 4, 128, (5000, 0, 2300), seed=21, block_size=64)
+    dv = to_device(inp)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    kw = dict(max_seq_len=inp["cap"], block_size=64, delta=2.5, sink=1, local=2, split_blocks=8,
+              sm_scale=sm_scale_for(128))
+    out_a, lse_a, mask_a = ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], out_dtype=torch.float32,
+                                      **{k_: v_ for k_, v_ in kw.items() if k_ != "block_size"})
+    ws = ffd.alloc_workspace(3, 16, 128, inp["cap"], 64, 8)
+    mask_b = torch.empty_like(mask_a)
+    out_b = torch.empty_like(out_a)
+    lse_b = torch.empty_like(lse_a)
+    ffd.ffd_decode_partials(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], kept_mask=mask_b, workspace=ws, **kw)
+    ffd.ffd_combine(dv["seq_lens"], max_seq_len=inp["cap"], block_size=64, split_blocks=8, workspace=ws, out=out_b,
+                    lse=lse_b)
+    torch.cuda.synchronize()
+    assert torch.equal(mask_a, mask_b)
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+    assert torch.isneginf(lse_b[1]).all() and (out_b[1] == 0).all()
