@@ -125,12 +125,12 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
           const bool ok = t < L;
           const uint8_t* src = kq + (size_t)(ok ? t : 0) * (D / 2) + ql * (D / 8);
           if constexpr (NCW == 4) {
-            cw[c][it] = ok ? *reinterpret_cast<const u32x4_t*>(src) : u32x4_t{0u, 0u, 0u, 0u};
+            cw[c][it] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
           } else {
             const uint2 u = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
             cw[c][it] = u32x4_t{u.x, u.y, 0u, 0u};
           }
-          sc[c][it] = ok ? ks[t] : 0.f;
+          sc[c][it] = ok ? __builtin_nontemporal_load(ks + t) : 0.f;
         }
       }
     }
@@ -327,7 +327,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       const int f = n * kWave + lane;        // chunk id within the tile
       const int r = f / VC, q = f % VC;
       const int t = min(t0 + r, tlast);
-      vr[n] = *reinterpret_cast<const u32x4_t*>(vb + (size_t)t * D + q * 8);
+      vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)t * D + q * 8));
     }
 
     // ---- QK on the matrix cores ----
