@@ -125,8 +125,8 @@ def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--delta", type=float, default=None, help="default: the workload's first delta")
     ap.add_argument("--no-cpu-baseline", action="store_true")
