@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """FFD decode benchmark on one MI355X.
 
-One step = one decode step of the whole batch: the fused scan -> Top-δ select
--> attend kernel (``ffd_decode_partials``) plus the split combine
-(``ffd_combine``). Inputs (bf16 q/K/V, the int4 key sketch) are built and
-resident in HBM before timing starts. Prints ONE JSON line.
+One step = one decode step of the whole batch, the work of ``ffd_decode``:
+the fused scan -> Top-δ select -> attend kernel (issued through
+``ffd_decode_partials``) and the split combine (``ffd_combine``), with a HIP
+event between them so the fused kernel is timed on its own. Inputs (bf16
+q/K/V, the int4 key sketch) are built and resident in HBM before timing
+starts. Prints ONE JSON line.
 
 Effective bandwidth counts algorithmic bytes: 68 B per valid token per kv
 head for the int4 scan (64 B codes + 4 B scale at d=128) plus 512 B (bf16 K
@@ -258,7 +260,7 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "fused_decode_kernel (ffd_decode_partials)",
+            "kernel": "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

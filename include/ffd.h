@@ -82,8 +82,9 @@ ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale,
                            const int32_t* pos_begin, const int32_t* pos_end,
                            int B, int Hkv, int cap, int d, int max_span, void* stream);
 
-/* Bytes of scratch that ffd_decode needs for these sizes (per-split partial
- * outputs and log-sum-exps, fp32). */
+/* Bytes of scratch that ffd_decode, ffd_decode_partials and ffd_combine need
+ * for these sizes: per-split partial outputs and log-sum-exps (fp32). 0 for
+ * unsupported sizes. */
 size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int block_size,
                                   int split_blocks);
 
@@ -131,11 +132,11 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *   kept_mask  uint8 [B, Hq, ceil(max_seq_len / block_size)] or NULL;
  *              1 = kept, 0 = dropped or past NB
  *   workspace  >= ffd_decode_workspace_bytes(B, Hq, d, max_seq_len,
- *              block_size, split_blocks) bytes, 256-byte aligned
+ *              block_size, split_blocks) bytes, 256-byte aligned, no
+ *              initialisation needed. Calls that share a workspace must not
+ *              overlap (calls on one stream never do).
  * A sequence with L == 0 gives out = 0, lse = -INFINITY and a zero mask row.
- * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8},
- * at most 4096 splits per sequence (ceil(ceil(max_seq_len / 64) /
- * split_blocks) <= 4096; FFD_ERR_UNSUPPORTED otherwise).
+ * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8}.
  * q, k, v, kq must be 16-byte aligned. Equivalent to ffd_decode_partials
  * followed by ffd_combine on the same stream.
  */
@@ -176,8 +177,7 @@ ffd_status ffd_decode_partials(const void* q, const void* k, const void* v,
  * over the splits written by ffd_decode_partials (same seq_lens,
  * max_seq_len, block_size and split_blocks; workspace laid out as described
  * there). A sequence with L == 0 gives out = 0 and lse = -INFINITY.
- * Supported: d in {64, 128}, block_size == 64, split_blocks in [1, 64],
- * at most 4096 splits per sequence.
+ * Supported: d in {64, 128}, block_size == 64, split_blocks in [1, 64].
  */
 ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, int d,
                        int block_size, int split_blocks, const void* workspace,

@@ -111,9 +111,6 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   }
   const int nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
-  if (ns > ffd::kMaxSplits)
-    return fail(FFD_ERR_UNSUPPORTED, "%s: %d splits per sequence exceed %d (raise split_blocks)", fn, ns,
-                ffd::kMaxSplits);
   const size_t need = (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
   if (need > 0) {
     if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);
@@ -228,9 +225,6 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   if (st != FFD_OK) return st;
   if (B > 0 && !seq_lens) return fail(FFD_ERR_INVALID_ARG, "%s: null seq_lens", fn);
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
-  if (ns > ffd::kMaxSplits)
-    return fail(FFD_ERR_UNSUPPORTED, "%s: %d splits per sequence exceed %d (raise split_blocks)", fn, ns,
-                ffd::kMaxSplits);
   const size_t need = (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
   if (need > 0) {
     if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);

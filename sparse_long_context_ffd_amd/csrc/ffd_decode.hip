@@ -37,7 +37,9 @@
 //                  through a per-wave XOR-swizzled LDS tile and read with the
 //                  transposing ds_read_b64_tr_b16, 2*2*(D/16) MFMAs per block.
 //  epilogue  wave partials merged through LDS; the split's normalised output
-//            and natural-log LSE go to workspace.
+//            and natural-log LSE go to workspace; a second, small kernel
+//            merges the splits (a merge inside this kernel needs device-scope
+//            publication of the partials, which measured slower on gfx950).
 #include <math.h>
 
 #include "ffd_device.h"
@@ -407,6 +409,30 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   }
 }
 
+// ---------------------------------------------------------------------------
+// split combine: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s
+// ---------------------------------------------------------------------------
+
+// Natural-log normaliser over the ns split LSEs at lp (one full wave).
+__device__ __forceinline__ float merged_lse(const float* lp, int ns, int lane) {
+  float mx = -INFINITY;
+  for (int s = lane; s < ns; s += kWave) mx = fmaxf(mx, lp[s]);
+  mx = wave_max_f(mx);
+  float den = 0.f;
+  for (int s = lane; s < ns; s += kWave) {
+    const float v = lp[s];
+    den += (v == -INFINITY) ? 0.f : expf(v - mx);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  return (ns > 0 && den > 0.f) ? mx + logf(den) : -INFINITY;
+}
+
+__device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, float v) {
+  if (p.out_f32) static_cast<float*>(p.out)[idx] = v;
+  else static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(v);
+}
+
 template <int D, int G, bool DENSE>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodeParams p) {
   __shared__ DecodeSmem<D, G> sm;
@@ -523,17 +549,20 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     p.o_part[row * D + cc] = num / den;
     if (cc == 0) p.lse_part[row] = (mx + log2f(den)) * kLn2;
   }
+
 }
 
 // ---------------------------------------------------------------------------
 // split combine: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s
 // ---------------------------------------------------------------------------
+// One workgroup per (sequence, query head): wave 0 forms the merged LSE; then
+// PARTS groups of D threads each sum an interleaved quarter of the splits
+// (four loads in flight per thread) and the parts are added in a fixed order.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(const DecodeParams p) {
-  constexpr int PARTS = 256 / D;   // split subsets summed in parallel
-  __shared__ float wgt[kMaxSplits];
-  __shared__ float red[PARTS][D];
+__global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
+  constexpr int PARTS = 512 / D;
   __shared__ float s_lse;
+  __shared__ float red[PARTS][D];
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
@@ -542,40 +571,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const DecodeParams p) {
   const size_t bh = (size_t)b * p.Hq + h;
   const float* lp = p.lse_part + bh * p.n_splits;
   const float* op = p.o_part + bh * p.n_splits * D;
-  // weights exp(lse_s - lse) of the splits, computed by wave 0
   if (tid < kWave) {
-    float mx = -INFINITY;
-    for (int s = tid; s < ns; s += kWave) mx = fmaxf(mx, lp[s]);
-    mx = wave_max_f(mx);
-    float den = 0.f;
-    for (int s = tid; s < ns; s += kWave) den += (lp[s] == -INFINITY) ? 0.f : expf(lp[s] - mx);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-    const float lse = (ns > 0 && den > 0.f) ? mx + logf(den) : -INFINITY;
-    for (int s = tid; s < ns; s += kWave) wgt[s] = (lse == -INFINITY) ? 0.f : expf(lp[s] - lse);
-    if (tid == 0) s_lse = lse;
+    const float l = merged_lse(lp, ns, tid);
+    if (tid == 0) s_lse = l;
   }
   __syncthreads();
+  const float lse = s_lse;
   const int c = tid % D, part = tid / D;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int s = part;
-  for (; s + 3 * PARTS < ns; s += 4 * PARTS) {
+  if (lse != -INFINITY) {
+    int s = part;
+    for (; s + 3 * PARTS < ns; s += 4 * PARTS) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += wgt[s + u * PARTS] * op[(size_t)(s + u * PARTS) * D + c];
+      for (int u = 0; u < 4; ++u) acc[u] += expf(lp[s + u * PARTS] - lse) * op[(size_t)(s + u * PARTS) * D + c];
+    }
+    for (; s < ns; s += PARTS) acc[0] += expf(lp[s] - lse) * op[(size_t)s * D + c];
   }
-  for (; s < ns; s += PARTS) acc[0] += wgt[s] * op[(size_t)s * D + c];
   red[part][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (part == 0) {
     float res = 0.f;
 #pragma unroll
     for (int q = 0; q < PARTS; ++q) res += red[q][c];
-    if (p.out_f32) {
-      static_cast<float*>(p.out)[bh * D + c] = res;
-    } else {
-      static_cast<uint16_t*>(p.out)[bh * D + c] = f32_to_bf16(res);
-    }
-    if (c == 0) p.lse[bh] = s_lse;
+    store_out(p, bh * D + c, res);
+    if (c == 0) p.lse[bh] = lse;
   }
 }
 
@@ -586,7 +605,7 @@ hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) 
     fused_decode_kernel<D, G, DENSE><<<grid, kThreads, 0, stream>>>(p);
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
-    combine_kernel<D><<<dim3(p.Hq, p.B), 256, 0, stream>>>(p);
+    combine_kernel<D><<<dim3(p.Hq, p.B), 512, 0, stream>>>(p);
   }
   return hipGetLastError();
 }

@@ -9,7 +9,6 @@ namespace ffd {
 
 constexpr int kBlockSize = 64;   // tokens per selection block
 constexpr int kMaxSplit = 64;    // max blocks per split (one workgroup)
-constexpr int kMaxSplits = 4096; // max splits per sequence (combine keeps their weights in LDS)
 constexpr size_t kWsAlign = 256;
 
 struct DecodeParams {
@@ -41,6 +40,7 @@ inline size_t ws_opart_bytes(int B, int Hq, int n_splits, int D) {
 inline size_t ws_lse_bytes(int B, int Hq, int n_splits) {
   return align_up((size_t)B * Hq * n_splits * sizeof(float), kWsAlign);
 }
+
 
 hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, const int32_t* pos_begin,
                               const int32_t* pos_end, int B, int Hkv, int cap, int D, int max_span,

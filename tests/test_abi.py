@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_workspace_bytes():
     ns = -(-(-(-131072 // 64)) // 32)
-    exp = 4 * 32 * ns * 128 * 4 + (-(-4 * 32 * ns * 4 // 256)) * 256
+    exp = 4 * 32 * ns * 128 * 4 + (-(-4 * 32 * ns * 4 // 256)) * 256   # partials, lse
     assert ffd.ffd_decode_workspace_bytes(4, 32, 128, 131072, 64, 32) == exp
     assert ffd.ffd_decode_workspace_bytes(4, 32, 128, 131072, 32, 32) == 0   # unsupported block size
     assert ffd.ffd_decode_workspace_bytes(0, 32, 128, 131072, 64, 32) == 0

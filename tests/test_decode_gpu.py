@@ -165,3 +165,70 @@ def test_partials_then_combine_equals_decode():
     assert torch.equal(mask_a, mask_b)
     assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
     assert torch.isneginf(lse_b[1]).all() and (out_b[1] == 0).all()
+
+
+def test_workspace_reused_across_calls_with_different_lengths():
+    """One workspace serves calls with different lengths (stale partials of an
+    earlier, longer call are never read)."""
+    say("decode: one workspace, several calls")
+    inp = make_random_inputs(3, 8, 2, 128, (7000, 300, 4100), seed=31, block_size=64)
+    dv = to_device(inp)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    ws = ffd.alloc_workspace(3, 8, 128, inp["cap"], 64, 4)
+    sm = sm_scale_for(128)
+    for lens in [(7000, 300, 4100), (64, 0, 4100), (6999, 300, 1), (7000, 300, 4100)]:
+        seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        a = ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, seq, delta=1.0, split_blocks=4, workspace=ws,
+                       out_dtype=torch.float32)
+        b = ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, seq, delta=1.0, split_blocks=4, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), lens
+        r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], np.array(lens), max_seq_len=inp["cap"],
+                                        block_size=64, delta=1.0, sink=1, local=4, split_blocks=4,
+                                        sm_scale=np.float32(sm))
+        assert_mask_equal(a[2].cpu().numpy(), r_mask, f"mask {lens}")
+        assert_close(a[0].cpu().numpy(), r_out, f"out {lens}")
+        assert_close(a[1].cpu().numpy(), r_lse, f"lse {lens}")
+
+
+def test_graph_capture_and_replay():
+    """ffd_decode allocates nothing and never synchronises, so it can be
+    captured in a HIP graph; every replay (with new query data copied in
+    between, eager work and syncs interleaved) matches an eager call."""
+    say("decode: HIP graph capture and replay")
+    inp = make_random_inputs(2, 16, 4, 128, (5000, 3000), seed=41, block_size=64)
+    dv = to_device(inp)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    torch.cuda.synchronize()
+    B, Hq, d = dv["q"].shape
+    msl = inp["cap"]
+    ws = ffd.alloc_workspace(B, Hq, d, msl, 64, 16)
+    q_static = dv["q"].clone()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    mask = torch.empty((B, Hq, -(-msl // 64)), dtype=torch.uint8, device="cuda")
+    kw = dict(max_seq_len=msl, block_size=64, delta=2.0, sink=1, local=2, split_blocks=16,
+              sm_scale=sm_scale_for(d))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm the stream before capture
+        ffd.ffd_decode(q_static, dv["k"], dv["v"], kq, ks, dv["seq_lens"], out=out, lse=lse, kept_mask=mask,
+                       workspace=ws, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ffd.ffd_decode(q_static, dv["k"], dv["v"], kq, ks, dv["seq_lens"], out=out, lse=lse, kept_mask=mask,
+                       workspace=ws, **kw)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for rep in range(4):
+        q_new = torch.randn(dv["q"].shape, device="cuda", generator=gen).to(torch.bfloat16)
+        q_static.copy_(q_new)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = ffd.decode(q_new, dv["k"], dv["v"], kq, ks, dv["seq_lens"], out_dtype=torch.float32,
+                         **{k_: v_ for k_, v_ in kw.items() if k_ != "block_size"})
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]), rep
+        assert torch.equal(lse, ref[1]), rep
+        assert torch.equal(mask, ref[2]), rep
