@@ -28,9 +28,13 @@ choice of this library, applied identically by the HIP path):
   scale 0 and all-zero codes.
 * A block's score is the maximum tentative score over its valid tokens
   ([TS] Methodology 3, "Top-δ Selection": blocks are filtered).
-* The pseudo-max m~ of [TS] Methodology 2 is, per query head, the maximum
-  block score inside the split of ``split_blocks`` consecutive blocks that one
-  workgroup owns; this needs no global reduction. The sink blocks (first
+* The pseudo-max m~ of [TS] Methodology 2 has two modes. "split" (default):
+  per query head, the maximum block score inside the split of
+  ``split_blocks`` consecutive blocks that one workgroup owns; this needs no
+  global reduction. "sink_local": per query head, the maximum block score over
+  the sink and local blocks, the estimate [TS] Methodology 2 (Pseudo-Max
+  Approximation) and 3 (Pseudo-max Estimation) describe; the kept set then
+  does not depend on the split size. In both modes the sink blocks (first
   ``sink``) and local blocks (last ``local``) are always kept.
 * δ is in natural-log logit units ([TS] Methodology 2, "Adaptivity"), the
   comparison is ``>=`` ([TS] Methodology 2, "Mechanism"), and the logit is
@@ -160,24 +164,39 @@ def block_scores(tok: np.ndarray, L: int, block_size: int) -> np.ndarray:
 # O5 + O6: split-local Top-δ with sink and local blocks   [TS] Methodology 2
 # --------------------------------------------------------------------------
 
-def select_blocks(scores: np.ndarray, split_blocks: int, delta, sink: int, local: int) -> np.ndarray:
-    """Keep block j iff score_j >= m~ - δ, where m~ is the maximum block score
-    in j's split (blocks [s*S, s*S+S)), or j is one of the first ``sink`` or
-    last ``local`` blocks. The subtraction and comparison run in the dtype of
-    ``scores`` (fp32 for the quantised scan)."""
+PSEUDO_MAX_MODES = ("split", "sink_local")
+
+
+def select_blocks(scores: np.ndarray, split_blocks: int, delta, sink: int, local: int,
+                  pseudo_max: str = "split") -> np.ndarray:
+    """Keep block j iff score_j >= m~ - δ, or j is one of the first ``sink`` or
+    last ``local`` blocks. m~ is the maximum block score in j's split (blocks
+    [s*S, s*S+S)) for ``pseudo_max="split"``, or the maximum over the sink and
+    local blocks for ``pseudo_max="sink_local"``. The subtraction and
+    comparison run in the dtype of ``scores`` (fp32 for the quantised scan)."""
+    if pseudo_max not in PSEUDO_MAX_MODES:
+        raise ValueError(f"pseudo_max must be one of {PSEUDO_MAX_MODES}")
     dt = scores.dtype.type
     nb = scores.shape[0]
     keep = np.zeros(nb, dtype=bool)
     d = dt(delta)
-    for s0 in range(0, nb, split_blocks):
-        seg = scores[s0:s0 + split_blocks]
-        m_tilde = dt(np.max(seg))
-        thr = dt(m_tilde - d)
-        keep[s0:s0 + split_blocks] = seg >= thr
-    keep[:min(sink, nb)] = True
+    forced = np.zeros(nb, dtype=bool)
+    forced[:min(sink, nb)] = True
     if local > 0:
-        keep[max(0, nb - local):] = True
-    return keep
+        forced[max(0, nb - local):] = True
+    if pseudo_max == "split":
+        for s0 in range(0, nb, split_blocks):
+            seg = scores[s0:s0 + split_blocks]
+            m_tilde = dt(np.max(seg))
+            thr = dt(m_tilde - d)
+            keep[s0:s0 + split_blocks] = seg >= thr
+    else:
+        if sink + local < 1:
+            raise ValueError("the sink/local pseudo-max needs sink + local >= 1")
+        m_tilde = dt(np.max(scores[forced]))
+        thr = dt(m_tilde - d)
+        keep = scores >= thr
+    return keep | forced
 
 
 # --------------------------------------------------------------------------
@@ -202,7 +221,7 @@ def attend(q64: np.ndarray, k64: np.ndarray, v64: np.ndarray, sm_scale) -> tuple
 
 def select_head(q32: np.ndarray, codes: np.ndarray, scale: np.ndarray, k64: np.ndarray, L: int,
                 block_size: int, delta, sink: int, local: int, split_blocks: int, sm_scale,
-                quantize: bool = True) -> np.ndarray:
+                quantize: bool = True, pseudo_max: str = "split") -> np.ndarray:
     """Kept-block mask of one query head over one sequence (O2-O6).
 
     With ``quantize=False`` the tentative scores are replaced by the exact fp64
@@ -213,11 +232,12 @@ def select_head(q32: np.ndarray, codes: np.ndarray, scale: np.ndarray, k64: np.n
     else:
         tok = float(sm_scale) * (k64[:L] @ q32.astype(np.float64))
     blk = block_scores(tok, L, block_size)
-    return select_blocks(blk, split_blocks, delta, sink, local)
+    return select_blocks(blk, split_blocks, delta, sink, local, pseudo_max)
 
 
 def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink: int, local: int,
-           split_blocks: int, sm_scale=None, quantize: bool = True, heads=None, mask_only: bool = False):
+           split_blocks: int, sm_scale=None, quantize: bool = True, heads=None, mask_only: bool = False,
+           pseudo_max: str = "split"):
     """One FFD decode step.
 
     ``q`` bf16 bits ``[B, Hq, d]``; ``k``, ``v`` bf16 bits ``[B, Hkv, cap, d]``;
@@ -229,6 +249,7 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
     token gives out 0, lse -inf and an all-zero mask row. ``heads`` restricts
     the work to a list of ``(b, h)`` pairs (other rows are left NaN / 0);
     ``mask_only`` skips the attention step (out and lse stay NaN).
+    ``pseudo_max`` picks how m~ is estimated (see :func:`select_blocks`).
     """
     q = np.asarray(q)
     B, Hq, d = q.shape
@@ -261,7 +282,7 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
             for h in hs:
                 q32 = bf16_bits_to_f32(q[b, h])
                 keep = select_head(q32, codes, scale, k64, L, block_size, delta, sink, local,
-                                   split_blocks, sm_scale, quantize)
+                                   split_blocks, sm_scale, quantize, pseudo_max)
                 mask[b, h, :keep.shape[0]] = keep
                 if mask_only:
                     continue
