@@ -99,7 +99,7 @@ def load_traffic(workload: str, delta: float, launches_bytes: float):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float):
+def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: str = "split"):
     """The oracle, as it stands, on a bounded sample of the same step: query
     heads of sequence 0, whole kv-head groups at a time, until ~budget_s."""
     import numpy as np
@@ -116,7 +116,7 @@ def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float):
             t0 = time.perf_counter()
             O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"], block_size=w.block_size,
                      delta=delta, sink=w.sink, local=w.local, split_blocks=w.split_blocks,
-                     sm_scale=np.float32(sm_scale), heads=heads)
+                     sm_scale=np.float32(sm_scale), heads=heads, pseudo_max=pseudo_max)
             t_total += time.perf_counter() - t0
             done_heads += heads
             if t_total >= budget_s:
@@ -131,6 +131,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--delta", type=float, default=None, help="default: the workload's first delta")
+    ap.add_argument("--pseudo-max", default="split", choices=["split", "sink_local"],
+                    help="split-local max (default) or the sink/local estimate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the delta=inf comparison")
@@ -207,7 +209,7 @@ def main() -> int:
             ev[0].record()
         ffd.ffd_decode_partials(q, k, v, None if math.isinf(dl) else kq, None if math.isinf(dl) else ks, seq,
                                 delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale, kept_mask=mask,
-                                workspace=ws, **kw)
+                                workspace=ws, pseudo_max=args.pseudo_max, **kw)
         if ev is not None:
             ev[1].record()
         ffd.ffd_combine(seq, workspace=ws, out=out, lse=lse, **kw)
@@ -256,7 +258,7 @@ def main() -> int:
             "workload": w.name, "batch": w.B, "seq_len": (list(w.lens) if w.lens else list(w.len_range)),
             "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "block_size": w.block_size,
             "delta": None if dense else delta, "sink_blocks": w.sink, "local_blocks": w.local,
-            "split_blocks": w.split_blocks, "out_dtype": "f32",
+            "split_blocks": w.split_blocks, "pseudo_max": args.pseudo_max, "out_dtype": "f32",
         },
         "roofline": {
             "bound": "hbm",
@@ -295,7 +297,7 @@ def main() -> int:
         }
 
     if not args.no_cpu_baseline:
-        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget)
+        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget, args.pseudo_max)
         smask = np.zeros_like(m)
         for b, h in heads:
             smask[b, h] = m[b, h]

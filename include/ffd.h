@@ -43,6 +43,14 @@ typedef enum {
 
 typedef enum { FFD_OUT_BF16 = 0, FFD_OUT_F32 = 1 } ffd_out_dtype;
 
+/* How the pseudo-max m~ of the Top-δ rule is estimated ([TS] Methodology 2). */
+typedef enum {
+  FFD_PSEUDO_MAX_SPLIT = 0,      /* max block score within the block's split (one workgroup) */
+  FFD_PSEUDO_MAX_SINK_LOCAL = 1  /* max block score over the sink and local blocks ([TS]
+                                    Methodology 2 "Pseudo-Max Approximation", 3 "Pseudo-max
+                                    Estimation"); the kept set does not depend on split_blocks */
+} ffd_pseudo_max;
+
 /* Version of this ABI (FFD_ABI_VERSION). */
 int ffd_abi_version(void);
 
@@ -106,10 +114,12 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *      tentative score is fl32(float(dot) * fl32(kscale_t * cq)), dot being
  *      the exact integer dot of the int8 query with the int4 codes; a block's
  *      score is the max over its valid tokens.
- *   3. Top-δ ([TS] Methodology 2, "Mechanism"): with m~ = the max block score
- *      in the block's split, block j is kept iff score_j >= fl32(m~ - delta),
- *      or j < sink_blocks, or j >= NB - local_blocks. δ is in natural-log
- *      logit units ([TS] Methodology 2, "Adaptivity").
+ *   3. Top-δ ([TS] Methodology 2, "Mechanism"): block j is kept iff
+ *      score_j >= fl32(m~ - delta), or j < sink_blocks, or j >= NB -
+ *      local_blocks. m~ is the max block score in j's split
+ *      (FFD_PSEUDO_MAX_SPLIT) or over the sink and local blocks
+ *      (FFD_PSEUDO_MAX_SINK_LOCAL). δ is in natural-log logit units ([TS]
+ *      Methodology 2, "Adaptivity").
  *   4. Refinement ([TS] Methodology 3, "Fine-Grained Refinement"): exact
  *      softmax attention (logit = sm_scale * q.k on the bf16 values, fp32
  *      accumulation) over the valid tokens of the kept blocks; per-split
@@ -124,7 +134,10 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *   max_seq_len host; bounds every L and sizes the grid and the mask
  *   delta      >= 0 (fp32), +INFINITY allowed
  *   sink_blocks, local_blocks >= 0
- *   split_blocks in [1, 64]; part of the semantics (the kept set depends on it)
+ *   pseudo_max FFD_PSEUDO_MAX_SPLIT or FFD_PSEUDO_MAX_SINK_LOCAL (the latter
+ *              needs 1 <= sink_blocks + local_blocks <= 64)
+ *   split_blocks in [1, 64]; with FFD_PSEUDO_MAX_SPLIT part of the semantics
+ *              (the kept set depends on it); otherwise only a work partition
  *   sm_scale   > 0 and finite (commonly fl32(1/sqrt(d)))
  *   out        [B, Hq, d], bf16 (round half to even) or f32 per out_dtype
  *   lse        f32 [B, Hq], natural log of the softmax normaliser over the
@@ -136,6 +149,8 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *              initialisation needed. Calls that share a workspace must not
  *              overlap (calls on one stream never do).
  * A sequence with L == 0 gives out = 0, lse = -INFINITY and a zero mask row.
+ * With FFD_PSEUDO_MAX_SINK_LOCAL a split may keep no block of a head; its
+ * partial then has lse = -INFINITY and weight 0 in the combine.
  * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8}.
  * q, k, v, kq must be 16-byte aligned. Equivalent to ffd_decode_partials
  * followed by ffd_combine on the same stream.
@@ -144,7 +159,7 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v,
                       const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
                       int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
                       int block_size, float delta, int sink_blocks, int local_blocks,
-                      int split_blocks, float sm_scale,
+                      int pseudo_max, int split_blocks, float sm_scale,
                       void* out, int out_dtype, float* lse, uint8_t* kept_mask,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -168,7 +183,7 @@ ffd_status ffd_decode_partials(const void* q, const void* k, const void* v,
                                const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
                                int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
                                int block_size, float delta, int sink_blocks, int local_blocks,
-                               int split_blocks, float sm_scale, uint8_t* kept_mask,
+                               int pseudo_max, int split_blocks, float sm_scale, uint8_t* kept_mask,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*

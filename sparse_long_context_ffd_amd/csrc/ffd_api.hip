@@ -78,7 +78,7 @@ namespace {
 ffd_status prepare_decode(const char* fn, const void* q, const void* k, const void* v, const uint8_t* kq,
                           const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv,
                           int d, int cap, int block_size, float delta, int sink_blocks, int local_blocks,
-                          int split_blocks, float sm_scale, uint8_t* kept_mask, void* workspace,
+                          int pseudo_max, int split_blocks, float sm_scale, uint8_t* kept_mask, void* workspace,
                           size_t workspace_bytes, ffd::DecodeParams& p, int& G, bool& dense) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || cap < 0 || max_seq_len < 0)
     return fail(FFD_ERR_INVALID_ARG, "%s: bad sizes (B=%d Hq=%d Hkv=%d cap=%d max_seq_len=%d)", fn, B, Hq, Hkv, cap,
@@ -93,12 +93,19 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   if (!(sm_scale > 0.f) || isinf(sm_scale))
     return fail(FFD_ERR_INVALID_ARG, "%s: sm_scale must be positive and finite (got %g)", fn, (double)sm_scale);
   if (block_size <= 0) return fail(FFD_ERR_INVALID_ARG, "%s: block_size must be positive (got %d)", fn, block_size);
+  if (pseudo_max != FFD_PSEUDO_MAX_SPLIT && pseudo_max != FFD_PSEUDO_MAX_SINK_LOCAL)
+    return fail(FFD_ERR_INVALID_ARG, "%s: unknown pseudo_max mode %d", fn, pseudo_max);
+  if (pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL && (long)sink_blocks + local_blocks < 1)
+    return fail(FFD_ERR_INVALID_ARG, "%s: the sink/local pseudo-max needs sink_blocks + local_blocks >= 1", fn);
   G = Hq / Hkv;
   if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
   if (block_size != ffd::kBlockSize) return fail(FFD_ERR_UNSUPPORTED, "%s: block_size=%d not supported (64)", fn, block_size);
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(FFD_ERR_UNSUPPORTED, "%s: group size %d not supported (1, 2, 4, 8)", fn, G);
   if (split_blocks > ffd::kMaxSplit)
     return fail(FFD_ERR_UNSUPPORTED, "%s: split_blocks=%d not supported (<= %d)", fn, split_blocks, ffd::kMaxSplit);
+  if (pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL && (long)sink_blocks + local_blocks > ffd::kMaxPseudoMax)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: sink_blocks + local_blocks = %ld exceeds %d with the sink/local pseudo-max",
+                fn, (long)sink_blocks + local_blocks, ffd::kMaxPseudoMax);
   if (B > 65535 || Hkv > 65535 || Hq > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B, Hq, Hkv must be <= 65535", fn);
   dense = isinf(delta);
   if (B > 0) {
@@ -140,6 +147,7 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.split_blocks = split_blocks;
   p.sink = sink_blocks;
   p.local = local_blocks;
+  p.pm_sink_local = pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL;
   p.delta = delta;
   p.sm_scale = sm_scale;
   return FFD_OK;
@@ -170,16 +178,16 @@ extern "C" {
 
 ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t* kq, const float* kscale,
                       const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
-                      int block_size, float delta, int sink_blocks, int local_blocks, int split_blocks,
-                      float sm_scale, void* out, int out_dtype, float* lse, uint8_t* kept_mask, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      int block_size, float delta, int sink_blocks, int local_blocks, int pseudo_max,
+                      int split_blocks, float sm_scale, void* out, int out_dtype, float* lse, uint8_t* kept_mask,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   ffd::DecodeParams p;
   int G;
   bool dense;
   ffd_status st = check_out_dtype("ffd_decode", out_dtype);
   if (st != FFD_OK) return st;
   st = prepare_decode("ffd_decode", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d, cap, block_size,
-                      delta, sink_blocks, local_blocks, split_blocks, sm_scale, kept_mask, workspace,
+                      delta, sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, workspace,
                       workspace_bytes, p, G, dense);
   if (st != FFD_OK) return st;
   st = check_out_ptrs("ffd_decode", B, out, lse);
@@ -193,14 +201,14 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
 ffd_status ffd_decode_partials(const void* q, const void* k, const void* v, const uint8_t* kq,
                                const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Hq,
                                int Hkv, int d, int cap, int block_size, float delta, int sink_blocks,
-                               int local_blocks, int split_blocks, float sm_scale, uint8_t* kept_mask,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               int local_blocks, int pseudo_max, int split_blocks, float sm_scale,
+                               uint8_t* kept_mask, void* workspace, size_t workspace_bytes, void* stream) {
   ffd::DecodeParams p;
   int G;
   bool dense;
   ffd_status st = prepare_decode("ffd_decode_partials", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d,
-                                 cap, block_size, delta, sink_blocks, local_blocks, split_blocks, sm_scale,
-                                 kept_mask, workspace, workspace_bytes, p, G, dense);
+                                 cap, block_size, delta, sink_blocks, local_blocks, pseudo_max, split_blocks,
+                                 sm_scale, kept_mask, workspace, workspace_bytes, p, G, dense);
   if (st != FFD_OK) return st;
   return launch("ffd_decode_partials", p, d, G, dense, ffd::Stage::kPartials, stream);
 }

@@ -59,8 +59,12 @@ struct DecodeSmem {
   int8_t qc[G][D];          // int8 scan query
   float cq[G];              // fl32(sq * sm_scale)
   int sumq[G];              // sum of qc (offset-binary correction)
-  float blk[kMaxSplit][G];  // block scores
-  float seed[G];            // split max m~ (natural-log units)
+  float blk[kMaxSplit][G];  // block scores of the split
+  int xidx[kMaxPseudoMax];  // sink/local blocks outside the split (sink/local pseudo-max)
+  int nx;
+  float xblk[kMaxPseudoMax][G];
+  float pm[G];              // sink/local pseudo-max per head
+  float seed[G];            // split max of the block scores (natural-log units)
   uint8_t kidx[kMaxSplit];  // kept blocks (split-local index)
   uint8_t khm[kMaxSplit];   // per-head keep bits of each kept block
   int nkept;
@@ -84,8 +88,11 @@ __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) 
 // Selection": stream the low-bit keys, compute tentative scores per block)
 // ---------------------------------------------------------------------------
 template <int D, int G>
+// Scores of `nblk` blocks: block j0 + i, or xlist[i] when xlist is given,
+// written to out[i][h].
 __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, size_t bh, int j0,
-                                            int nblk, int L, int lane, int w) {
+                                            const int* xlist, float (*out)[G], int nblk, int L, int lane,
+                                            int w) {
   constexpr int NCW = D / 32;  // 32-bit code words per lane (8 codes each)
   const int quad = lane >> 2;
   const int ql = lane & 3;
@@ -120,7 +127,7 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
       if (jl < nblk) {
-        const int t0 = (j0 + jl) * kBlockSize;
+        const int t0 = (xlist ? xlist[jl] : j0 + jl) * kBlockSize;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int t = t0 + it * 16 + quad;
@@ -140,7 +147,7 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
       if (jl >= nblk) continue;
-      const int t0 = (j0 + jl) * kBlockSize;
+      const int t0 = (xlist ? xlist[jl] : j0 + jl) * kBlockSize;
       float bm[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
@@ -181,7 +188,7 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
       }
       if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) sm.blk[jl][h] = bm[h];
+        for (int h = 0; h < G; ++h) out[jl][h] = bm[h];
       }
     }
   }
@@ -207,8 +214,9 @@ __device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<
     const bool forced = jb < p.sink || jb >= NB - p.local;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mt = wave_max_f(s[h]);
-      const float thr = mt - p.delta;
+      const float mt = wave_max_f(s[h]);   // split max: the pseudo-max in split mode, else the seed
+      const float pm = p.pm_sink_local ? sm.pm[h] : mt;
+      const float thr = pm - p.delta;
       if (in_split && (s[h] >= thr || forced)) hm |= 1u << h;
       if (lane == 0) sm.seed[h] = mt;
     }
@@ -501,7 +509,33 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 
   // ---- scan + select ------------------------------------------------------
   if constexpr (!DENSE) {
-    scan_blocks<D, G>(p, sm, bh, j0, nblk, L, lane, w);
+    scan_blocks<D, G>(p, sm, bh, j0, nullptr, sm.blk, nblk, L, lane, w);
+    if (p.pm_sink_local) {
+      // the sink and local blocks that lie outside this split are scanned too
+      if (tid == 0) {
+        int nx = 0;
+        const int s_end = min(p.sink, NB);
+        const int l_beg = max(s_end, NB - p.local);
+        for (int jb = 0; jb < s_end; ++jb)
+          if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
+        for (int jb = l_beg; jb < NB; ++jb)
+          if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
+        sm.nx = nx;
+      }
+      __syncthreads();
+      const int nx = sm.nx;
+      scan_blocks<D, G>(p, sm, bh, 0, sm.xidx, sm.xblk, nx, L, lane, w);
+      __syncthreads();
+      if (tid < G) {
+        float m = -INFINITY;
+        for (int x = 0; x < nx; ++x) m = fmaxf(m, sm.xblk[x][tid]);
+        for (int jl = 0; jl < nblk; ++jl) {
+          const int jb = j0 + jl;
+          if (jb < p.sink || jb >= NB - p.local) m = fmaxf(m, sm.blk[jl][tid]);
+        }
+        sm.pm[tid] = m;
+      }
+    }
     __syncthreads();
   }
   if (w == 0) select_blocks<D, G, DENSE>(p, sm, b, j, j0, nblk, nmask, NB, lane);
@@ -546,8 +580,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
       num += sm.wo[ww][h][cc] * a;
     }
     const size_t row = ((size_t)b * p.Hq + (size_t)j * G + h) * p.n_splits + split;
-    p.o_part[row * D + cc] = num / den;
-    if (cc == 0) p.lse_part[row] = (mx + log2f(den)) * kLn2;
+    // a split can keep no block of a head (sink/local pseudo-max): empty partial
+    p.o_part[row * D + cc] = den > 0.f ? num / den : 0.f;
+    if (cc == 0) p.lse_part[row] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
   }
 
 }

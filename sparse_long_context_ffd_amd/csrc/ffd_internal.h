@@ -9,6 +9,7 @@ namespace ffd {
 
 constexpr int kBlockSize = 64;   // tokens per selection block
 constexpr int kMaxSplit = 64;    // max blocks per split (one workgroup)
+constexpr int kMaxPseudoMax = 64; // max sink + local blocks with the sink/local pseudo-max
 constexpr size_t kWsAlign = 256;
 
 struct DecodeParams {
@@ -29,6 +30,7 @@ struct DecodeParams {
   int n_splits;            // ceil(nb_max / split_blocks)
   int split_blocks;
   int sink, local;
+  int pm_sink_local;       // 1: pseudo-max over the sink/local blocks; 0: split max
   float delta, sm_scale;
 };
 

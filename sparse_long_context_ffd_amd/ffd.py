@@ -30,6 +30,7 @@ FFD_ERR_WORKSPACE = 3
 FFD_ERR_HIP = 4
 FFD_OUT_BF16 = 0
 FFD_OUT_F32 = 1
+PSEUDO_MAX = {"split": 0, "sink_local": 1}
 
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_decode_workspace_bytes",
                     "ffd_decode", "ffd_decode_partials", "ffd_combine")
@@ -67,13 +68,13 @@ def lib() -> ctypes.CDLL:
     L.ffd_decode.restype = _i
     L.ffd_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,          # q k v kq kscale seq_lens
                              _i, _i, _i, _i, _i, _i,                # max_seq_len B Hq Hkv d cap
-                             _i, ctypes.c_float, _i, _i, _i,        # block_size delta sink local split
+                             _i, ctypes.c_float, _i, _i, _i, _i,    # block_size delta sink local pm split
                              ctypes.c_float,                        # sm_scale
                              _vp, _i, _vp, _vp,                     # out out_dtype lse mask
                              _vp, ctypes.c_size_t, _vp]             # workspace bytes stream
     L.ffd_decode_partials.restype = _i
     L.ffd_decode_partials.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
-                                      _i, ctypes.c_float, _i, _i, _i, ctypes.c_float,
+                                      _i, ctypes.c_float, _i, _i, _i, _i, ctypes.c_float,
                                       _vp, _vp, ctypes.c_size_t, _vp]
     L.ffd_combine.restype = _i
     L.ffd_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _i, _vp, _vp]
@@ -165,6 +166,12 @@ def _check_outputs(out, lse, B, Hq, d):
     return FFD_OUT_F32 if out.dtype == torch.float32 else FFD_OUT_BF16
 
 
+def _pm(pseudo_max) -> int:
+    if pseudo_max not in PSEUDO_MAX:
+        raise ValueError(f"pseudo_max must be one of {tuple(PSEUDO_MAX)}")
+    return PSEUDO_MAX[pseudo_max]
+
+
 def _ws(workspace):
     return 0 if workspace is None else workspace.numel() * workspace.element_size()
 
@@ -173,24 +180,27 @@ def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[t
                kscale: Optional[torch.Tensor], seq_lens: torch.Tensor, *, max_seq_len: int, block_size: int,
                delta: float, sink: int, local: int, split_blocks: int, sm_scale: float, out: torch.Tensor,
                lse: torch.Tensor, kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
-               stream=None) -> None:
+               pseudo_max: str = "split", stream=None) -> None:
     """One decode step into preallocated ``out`` / ``lse`` / ``kept_mask``."""
     B, Hq, Hkv, d, cap = _check_decode_inputs(q, k, v, kq, kscale, seq_lens, max_seq_len, block_size, kept_mask)
     odt = _check_outputs(out, lse, B, Hq, d)
     _check(lib().ffd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
                             int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta), int(sink),
-                            int(local), int(split_blocks), float(sm_scale), _ptr(out), odt, _ptr(lse),
+                            int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out), odt,
+                            _ptr(lse),
                             _ptr(kept_mask), _ptr(workspace), _ws(workspace), _stream(stream)))
 
 
 def ffd_decode_partials(q, k, v, kq, kscale, seq_lens, *, max_seq_len: int, block_size: int, delta: float,
                         sink: int, local: int, split_blocks: int, sm_scale: float,
-                        kept_mask: Optional[torch.Tensor], workspace: torch.Tensor, stream=None) -> None:
+                        kept_mask: Optional[torch.Tensor], workspace: torch.Tensor, pseudo_max: str = "split",
+                        stream=None) -> None:
     """The fused scan -> select -> attend kernel alone; partials stay in ``workspace``."""
     B, Hq, Hkv, d, cap = _check_decode_inputs(q, k, v, kq, kscale, seq_lens, max_seq_len, block_size, kept_mask)
     _check(lib().ffd_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
                                      int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta),
-                                     int(sink), int(local), int(split_blocks), float(sm_scale), _ptr(kept_mask),
+                                     int(sink), int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale),
+                                     _ptr(kept_mask),
                                      _ptr(workspace), _ws(workspace), _stream(stream)))
 
 
@@ -234,7 +244,7 @@ def alloc_workspace(B: int, Hq: int, d: int, max_seq_len: int, block_size: int =
 def decode(q, k, v, kq, kscale, seq_lens, *, max_seq_len: Optional[int] = None, block_size: int = 64,
            delta: float = 6.0, sink: int = 1, local: int = 4, split_blocks: int = 32,
            sm_scale: Optional[float] = None, out_dtype=torch.bfloat16, with_mask: bool = True,
-           workspace: Optional[torch.Tensor] = None, stream=None):
+           workspace: Optional[torch.Tensor] = None, pseudo_max: str = "split", stream=None):
     """Allocate outputs and run one decode step; returns ``(out, lse, kept_mask)``."""
     B, Hq, d = q.shape
     if max_seq_len is None:
@@ -249,5 +259,5 @@ def decode(q, k, v, kq, kscale, seq_lens, *, max_seq_len: Optional[int] = None, 
         workspace = alloc_workspace(B, Hq, d, max_seq_len, block_size, split_blocks, q.device)
     ffd_decode(q, k, v, kq, kscale, seq_lens, max_seq_len=max_seq_len, block_size=block_size, delta=delta,
                sink=sink, local=local, split_blocks=split_blocks, sm_scale=sm_scale, out=out, lse=lse,
-               kept_mask=mask, workspace=workspace, stream=stream)
+               kept_mask=mask, workspace=workspace, pseudo_max=pseudo_max, stream=stream)
     return out, lse, mask

@@ -38,12 +38,12 @@ def sm_scale_for(d: int) -> float:
 
 
 def run_gpu(dv: dict, *, max_seq_len: int, delta: float, sink: int, local: int, split_blocks: int,
-            sm_scale: float, out_dtype=torch.float32, kq=None, kscale=None):
+            sm_scale: float, out_dtype=torch.float32, kq=None, kscale=None, pseudo_max: str = "split"):
     if kq is None and not math.isinf(delta):
         kq, kscale = ffd.quantize_kv(dv["k"], dv["seq_lens"])
     out, lse, mask = ffd.decode(dv["q"], dv["k"], dv["v"], kq, kscale, dv["seq_lens"], max_seq_len=max_seq_len,
                                 block_size=64, delta=delta, sink=sink, local=local, split_blocks=split_blocks,
-                                sm_scale=sm_scale, out_dtype=out_dtype)
+                                sm_scale=sm_scale, out_dtype=out_dtype, pseudo_max=pseudo_max)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), mask.cpu().numpy()
 

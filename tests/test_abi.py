@@ -45,13 +45,13 @@ def test_workspace_bytes():
 
 def _decode(**kw):
     args = dict(q=None, k=None, v=None, kq=None, kscale=None, seq_lens=None, max_seq_len=128, B=1, Hq=4, Hkv=1,
-                d=128, cap=128, block_size=64, delta=6.0, sink=1, local=4, split=32, sm_scale=0.088388,
+                d=128, cap=128, block_size=64, delta=6.0, sink=1, local=4, pm=0, split=32, sm_scale=0.088388,
                 out=None, out_dtype=0, lse=None, mask=None, ws=None, ws_bytes=0, stream=None)
     args.update(kw)
     L = ffd.lib()
     return L.ffd_decode(args["q"], args["k"], args["v"], args["kq"], args["kscale"], args["seq_lens"],
                         args["max_seq_len"], args["B"], args["Hq"], args["Hkv"], args["d"], args["cap"],
-                        args["block_size"], ctypes.c_float(args["delta"]), args["sink"], args["local"],
+                        args["block_size"], ctypes.c_float(args["delta"]), args["sink"], args["local"], args["pm"],
                         args["split"], ctypes.c_float(args["sm_scale"]), args["out"], args["out_dtype"],
                         args["lse"], args["mask"], args["ws"], args["ws_bytes"], args["stream"])
 
@@ -71,6 +71,9 @@ def _decode(**kw):
     (dict(block_size=32), ffd.FFD_ERR_UNSUPPORTED, "block_size"),
     (dict(Hq=12, Hkv=4), ffd.FFD_ERR_UNSUPPORTED, "group size"),
     (dict(split=65), ffd.FFD_ERR_UNSUPPORTED, "split_blocks"),
+    (dict(pm=2), ffd.FFD_ERR_INVALID_ARG, "pseudo_max"),
+    (dict(pm=1, sink=0, local=0), ffd.FFD_ERR_INVALID_ARG, "sink/local"),
+    (dict(pm=1, sink=40, local=30), ffd.FFD_ERR_UNSUPPORTED, "exceeds"),
     (dict(), ffd.FFD_ERR_INVALID_ARG, "null"),
 ])
 def test_host_validation(kw, status, needle):
