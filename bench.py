@@ -100,8 +100,8 @@ def load_traffic(workload: str, delta: float, launches_bytes: float):
 
 
 def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: str = "split"):
-    """The oracle, as it stands, on a bounded sample of the same step: query
-    heads of sequence 0, whole kv-head groups at a time, until ~budget_s."""
+    """The oracle, as it stands, on a bounded sample of the same step: whole
+    (sequence, kv head) groups in order, until ~budget_s of work is done."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -111,16 +111,18 @@ def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: st
     done_heads = []
     t_total = 0.0
     with threadpool_limits(limits=1):
-        for j in range(w.Hkv):
-            heads = [(0, h) for h in range(j * G, (j + 1) * G)]
-            t0 = time.perf_counter()
-            O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"], block_size=w.block_size,
-                     delta=delta, sink=w.sink, local=w.local, split_blocks=w.split_blocks,
-                     sm_scale=np.float32(sm_scale), heads=heads, pseudo_max=pseudo_max)
-            t_total += time.perf_counter() - t0
-            done_heads += heads
-            if t_total >= budget_s:
-                break
+        for b in range(w.B):
+            for j in range(w.Hkv):
+                heads = [(b, h) for h in range(j * G, (j + 1) * G)]
+                t0 = time.perf_counter()
+                O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
+                         block_size=w.block_size, delta=delta, sink=w.sink, local=w.local,
+                         split_blocks=w.split_blocks, sm_scale=np.float32(sm_scale), heads=heads,
+                         pseudo_max=pseudo_max)
+                t_total += time.perf_counter() - t0
+                done_heads += heads
+                if t_total >= budget_s:
+                    return t_total, done_heads
     return t_total, done_heads
 
 
@@ -314,11 +316,11 @@ def main() -> int:
             "unit": "GB/s",
             "cores": 1,
             "kind": "oracle",
-            "sample": (f"sequence 0, {len(groups)} of {w.B * w.Hkv} (sequence, kv head) groups "
+            "sample": (f"{len(groups)} of {w.B * w.Hkv} (sequence, kv head) groups of the same step "
                        f"({len(heads)} query heads); NumPy oracle incl. its int4 key quantisation, "
                        "single thread"),
             "seconds": round(t_cpu, 2),
-            "us_per_step_extrapolated": round(t_cpu / len(groups) * (w.B * w.Hkv) * 1e6, 0),
+            "us_per_step_extrapolated": round(t_cpu / sample_b * alg_bytes * 1e6, 0),
             "host_cpu": host_cpu_model(),
             "host_cpu_count": os.cpu_count(),
             "host_affinity": len(os.sched_getaffinity(0)),
