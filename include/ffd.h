@@ -90,6 +90,20 @@ ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale,
                            const int32_t* pos_begin, const int32_t* pos_end,
                            int B, int Hkv, int cap, int d, int max_span, void* stream);
 
+/*
+ * ffd_quantize_kv_paged -- ffd_quantize_kv for a paged cache. A page holds one
+ * 64-token block of every kv head: K pages bf16 [num_pages, Hkv, 64, d], kq
+ * pages uint8 [num_pages, Hkv, 64, d/2], kscale pages f32 [num_pages, Hkv,
+ * 64]. Token t of sequence b lives in page block_table[b * table_stride + t/64]
+ * (int32, device), row t % 64. Tokens at or past table_stride * 64 are not
+ * processed; page numbers outside [0, num_pages) are clamped (never fault).
+ * Same arithmetic and output bytes as ffd_quantize_kv.
+ */
+ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* kscale_pages,
+                                 const int32_t* block_table, int table_stride, int num_pages,
+                                 const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int d,
+                                 int max_span, void* stream);
+
 /* Bytes of scratch that ffd_decode, ffd_decode_partials and ffd_combine need
  * for these sizes: per-split partial outputs and log-sum-exps (fp32). 0 for
  * unsupported sizes. */
@@ -162,6 +176,24 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v,
                       int pseudo_max, int split_blocks, float sm_scale,
                       void* out, int out_dtype, float* lse, uint8_t* kept_mask,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ffd_decode_paged -- ffd_decode on a paged KV cache (a block table instead of
+ * one contiguous cache per sequence, as serving engines keep it). Pages are laid
+ * out as for ffd_quantize_kv_paged (K and V pages bf16 [num_pages, Hkv, 64, d]);
+ * block j of sequence b is page block_table[b * table_stride + j], for
+ * j < ceil(L / 64); table_stride >= ceil(max_seq_len / 64). Page numbers
+ * outside [0, num_pages) are clamped. Same semantics, results and workspace as
+ * ffd_decode: a paged cache holding the same rows gives bit-identical outputs.
+ */
+ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const uint8_t* kq_pages, const float* kscale_pages,
+                            const int32_t* block_table, int table_stride, int num_pages,
+                            const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d,
+                            int block_size, float delta, int sink_blocks, int local_blocks,
+                            int pseudo_max, int split_blocks, float sm_scale,
+                            void* out, int out_dtype, float* lse, uint8_t* kept_mask,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * ffd_decode_partials -- the first half of ffd_decode: the fused scan ->

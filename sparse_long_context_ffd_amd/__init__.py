@@ -20,10 +20,12 @@ from .ffd import (  # noqa: F401
     ffd_abi_version,
     ffd_combine,
     ffd_decode,
+    ffd_decode_paged,
     ffd_decode_partials,
     ffd_decode_workspace_bytes,
     ffd_last_error,
     ffd_quantize_kv,
+    ffd_quantize_kv_paged,
     lib,
     quantize_kv,
 )

@@ -43,23 +43,54 @@ int ffd_abi_version(void) { return FFD_ABI_VERSION; }
 
 const char* ffd_last_error(void) { return g_err.c_str(); }
 
+}  // extern "C"
+
+namespace {
+
+ffd_status quantize_common(const char* fn, const void* k, uint8_t* kq, float* kscale, const int32_t* pos_begin,
+                           const int32_t* pos_end, const int32_t* block_table, int table_stride, int num_pages,
+                           int B, int Hkv, int cap, int d, int max_span, void* stream) {
+  if (B < 0 || Hkv < 0 || cap < 0 || max_span < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: negative size (B=%d Hkv=%d cap=%d max_span=%d)", fn, B, Hkv, cap, max_span);
+  if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
+  if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
+  if (B == 0 || Hkv == 0 || cap == 0 || max_span == 0) return ok();
+  if (!k || !kq || !kscale || !pos_begin || !pos_end) return fail(FFD_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(k) || !aligned16(kq)) return fail(FFD_ERR_INVALID_ARG, "%s: k and kq must be 16-byte aligned", fn);
+  if (B > 65535 || Hkv > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B and Hkv must be <= 65535", fn);
+  hipError_t e = ffd::launch_quantize_kv(static_cast<const uint16_t*>(k), kq, kscale, pos_begin, pos_end, block_table,
+                                         table_stride, num_pages, B, Hkv, cap, d, max_span,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FFD_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale, const int32_t* pos_begin,
                            const int32_t* pos_end, int B, int Hkv, int cap, int d, int max_span,
                            void* stream) {
-  if (B < 0 || Hkv < 0 || cap < 0 || max_span < 0)
-    return fail(FFD_ERR_INVALID_ARG, "ffd_quantize_kv: negative size (B=%d Hkv=%d cap=%d max_span=%d)", B, Hkv,
-                cap, max_span);
-  if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "ffd_quantize_kv: d must be positive and even (d=%d)", d);
-  if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "ffd_quantize_kv: d=%d not supported (64, 128)", d);
-  if (B == 0 || Hkv == 0 || cap == 0 || max_span == 0) return ok();
-  if (!k || !kq || !kscale || !pos_begin || !pos_end)
-    return fail(FFD_ERR_INVALID_ARG, "ffd_quantize_kv: null pointer argument");
-  if (!aligned16(k) || !aligned16(kq)) return fail(FFD_ERR_INVALID_ARG, "ffd_quantize_kv: k and kq must be 16-byte aligned");
-  if (B > 65535 || Hkv > 65535) return fail(FFD_ERR_UNSUPPORTED, "ffd_quantize_kv: B and Hkv must be <= 65535");
-  hipError_t e = ffd::launch_quantize_kv(static_cast<const uint16_t*>(k), kq, kscale, pos_begin, pos_end, B, Hkv,
-                                         cap, d, max_span, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(FFD_ERR_HIP, "ffd_quantize_kv: launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return quantize_common("ffd_quantize_kv", k, kq, kscale, pos_begin, pos_end, nullptr, 0, 0, B, Hkv, cap, d,
+                         max_span, stream);
+}
+
+ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* kscale_pages,
+                                 const int32_t* block_table, int table_stride, int num_pages,
+                                 const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int d,
+                                 int max_span, void* stream) {
+  const char* fn = "ffd_quantize_kv_paged";
+  if (table_stride < 0 || num_pages < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: negative table_stride/num_pages (%d, %d)", fn, table_stride, num_pages);
+  if (B > 0 && Hkv > 0 && max_span > 0 && table_stride > 0 && num_pages > 0 && !block_table)
+    return fail(FFD_ERR_INVALID_ARG, "%s: null block_table", fn);
+  if (table_stride == 0 || num_pages == 0) {   // nothing addressable
+    if (B < 0 || Hkv < 0 || max_span < 0) return fail(FFD_ERR_INVALID_ARG, "%s: negative size", fn);
+    return ok();
+  }
+  return quantize_common(fn, k_pages, kq_pages, kscale_pages, pos_begin, pos_end, block_table, table_stride,
+                         num_pages, B, Hkv, table_stride * ffd::kBlockSize, d, max_span, stream);
 }
 
 size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int block_size, int split_blocks) {
@@ -79,13 +110,21 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
                           const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv,
                           int d, int cap, int block_size, float delta, int sink_blocks, int local_blocks,
                           int pseudo_max, int split_blocks, float sm_scale, uint8_t* kept_mask, void* workspace,
-                          size_t workspace_bytes, ffd::DecodeParams& p, int& G, bool& dense) {
+                          size_t workspace_bytes, const int32_t* block_table, int table_stride, int num_pages,
+                          ffd::DecodeParams& p, int& G, bool& dense) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || cap < 0 || max_seq_len < 0)
     return fail(FFD_ERR_INVALID_ARG, "%s: bad sizes (B=%d Hq=%d Hkv=%d cap=%d max_seq_len=%d)", fn, B, Hq, Hkv, cap,
                 max_seq_len);
   if (Hq % Hkv) return fail(FFD_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
-  if (cap < max_seq_len) return fail(FFD_ERR_INVALID_ARG, "%s: cap=%d < max_seq_len=%d", fn, cap, max_seq_len);
+  if (block_table == nullptr && cap < max_seq_len)
+    return fail(FFD_ERR_INVALID_ARG, "%s: cap=%d < max_seq_len=%d", fn, cap, max_seq_len);
+  if (block_table != nullptr) {
+    const long nbm = ((long)max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
+    if (table_stride < nbm)
+      return fail(FFD_ERR_INVALID_ARG, "%s: table_stride=%d < ceil(max_seq_len/64)=%ld", fn, table_stride, nbm);
+    if (num_pages < 1) return fail(FFD_ERR_INVALID_ARG, "%s: num_pages must be >= 1 (got %d)", fn, num_pages);
+  }
   if (isnan(delta) || delta < 0.f) return fail(FFD_ERR_INVALID_ARG, "%s: delta must be >= 0 (got %g)", fn, (double)delta);
   if (sink_blocks < 0 || local_blocks < 0)
     return fail(FFD_ERR_INVALID_ARG, "%s: sink/local must be >= 0 (%d, %d)", fn, sink_blocks, local_blocks);
@@ -133,6 +172,9 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.kq = kq;
   p.kscale = kscale;
   p.seq_lens = seq_lens;
+  p.block_table = block_table;
+  p.table_stride = table_stride;
+  p.num_pages = num_pages;
   char* ws = static_cast<char*>(workspace);
   p.o_part = need ? reinterpret_cast<float*>(ws) : nullptr;
   p.lse_part = need ? reinterpret_cast<float*>(ws + ffd::ws_opart_bytes(B, Hq, ns, d)) : nullptr;
@@ -188,7 +230,7 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
   if (st != FFD_OK) return st;
   st = prepare_decode("ffd_decode", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d, cap, block_size,
                       delta, sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, workspace,
-                      workspace_bytes, p, G, dense);
+                      workspace_bytes, nullptr, 0, 0, p, G, dense);
   if (st != FFD_OK) return st;
   st = check_out_ptrs("ffd_decode", B, out, lse);
   if (st != FFD_OK) return st;
@@ -196,6 +238,32 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
   p.lse = lse;
   p.out_f32 = out_dtype == FFD_OUT_F32;
   return launch("ffd_decode", p, d, G, dense, ffd::Stage::kBoth, stream);
+}
+
+ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pages, const uint8_t* kq_pages,
+                            const float* kscale_pages, const int32_t* block_table, int table_stride, int num_pages,
+                            const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d,
+                            int block_size, float delta, int sink_blocks, int local_blocks, int pseudo_max,
+                            int split_blocks, float sm_scale, void* out, int out_dtype, float* lse,
+                            uint8_t* kept_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "ffd_decode_paged";
+  if (max_seq_len > 0 && B > 0 && !block_table) return fail(FFD_ERR_INVALID_ARG, "%s: null block_table", fn);
+  ffd::DecodeParams p;
+  int G;
+  bool dense;
+  ffd_status st = check_out_dtype(fn, out_dtype);
+  if (st != FFD_OK) return st;
+  const int32_t* table = (max_seq_len > 0 && B > 0) ? block_table : nullptr;
+  st = prepare_decode(fn, q, k_pages, v_pages, kq_pages, kscale_pages, seq_lens, max_seq_len, B, Hq, Hkv, d,
+                      max_seq_len, block_size, delta, sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale,
+                      kept_mask, workspace, workspace_bytes, table, table_stride, num_pages, p, G, dense);
+  if (st != FFD_OK) return st;
+  st = check_out_ptrs(fn, B, out, lse);
+  if (st != FFD_OK) return st;
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = out_dtype == FFD_OUT_F32;
+  return launch(fn, p, d, G, dense, ffd::Stage::kBoth, stream);
 }
 
 ffd_status ffd_decode_partials(const void* q, const void* k, const void* v, const uint8_t* kq,
@@ -208,7 +276,7 @@ ffd_status ffd_decode_partials(const void* q, const void* k, const void* v, cons
   bool dense;
   ffd_status st = prepare_decode("ffd_decode_partials", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d,
                                  cap, block_size, delta, sink_blocks, local_blocks, pseudo_max, split_blocks,
-                                 sm_scale, kept_mask, workspace, workspace_bytes, p, G, dense);
+                                 sm_scale, kept_mask, workspace, workspace_bytes, nullptr, 0, 0, p, G, dense);
   if (st != FFD_OK) return st;
   return launch("ffd_decode_partials", p, d, G, dense, ffd::Stage::kPartials, stream);
 }

@@ -90,7 +90,7 @@ __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) 
 template <int D, int G>
 // Scores of `nblk` blocks: block j0 + i, or xlist[i] when xlist is given,
 // written to out[i][h].
-__device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, size_t bh, int j0,
+__device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
                                             const int* xlist, float (*out)[G], int nblk, int L, int lane,
                                             int w) {
   constexpr int NCW = D / 32;  // 32-bit code words per lane (8 codes each)
@@ -114,8 +114,6 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
     corr[h] = 8 * sm.sumq[h];
     cq[h] = sm.cq[h];
   }
-  const uint8_t* kq = p.kq + bh * (size_t)p.cap * (D / 2);
-  const float* ks = p.kscale + bh * (size_t)p.cap;
 
   // Each wave owns blocks w, w+4, w+8, ...; kChunk of them are loaded at once
   // (kChunk*4 KiB of codes in flight per wave) before any is reduced.
@@ -127,19 +125,23 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
       if (jl < nblk) {
-        const int t0 = (xlist ? xlist[jl] : j0 + jl) * kBlockSize;
+        const int jb = xlist ? xlist[jl] : j0 + jl;
+        const int t0 = jb * kBlockSize;
+        const size_t r0 = cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
+        const uint8_t* kq = p.kq + r0 * (D / 2);
+        const float* ks = p.kscale + r0;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int t = t0 + it * 16 + quad;
           const bool ok = t < L;
-          const uint8_t* src = kq + (size_t)(ok ? t : 0) * (D / 2) + ql * (D / 8);
+          const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * (D / 2) + ql * (D / 8);
           if constexpr (NCW == 4) {
             cw[c][it] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
           } else {
             const uint2 u = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
             cw[c][it] = u32x4_t{u.x, u.y, 0u, 0u};
           }
-          sc[c][it] = ok ? __builtin_nontemporal_load(ks + t) : 0.f;
+          sc[c][it] = ok ? __builtin_nontemporal_load(ks + (t - t0)) : 0.f;
         }
       }
     }
@@ -273,8 +275,8 @@ struct AttendState {
 };
 
 template <int D, int G, bool DENSE>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, size_t bh, int b,
-                                              int j, int j0, int L, int lane, int w, AttendState<D>& st) {
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
+                                              int L, int lane, int w, AttendState<D>& st) {
   constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
   constexpr int NT = D / 16;    // MFMA n-tiles of the output
   constexpr int VC = D / 8;     // 16-byte chunks per V row
@@ -298,8 +300,6 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   st.m = (h < G) ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
   st.l = 0.f;
 
-  const uint16_t* kb = p.k + bh * (size_t)p.cap * D;
-  const uint16_t* vb = p.v + bh * (size_t)p.cap * D;
   char* vt = reinterpret_cast<char*>(sm.vt[w]);
   // LDS addresses of the V tile. Store: 16-byte chunk n*64 + lane of the tile
   // goes to wbase[n & 1] + (n >> 1) * 2048 (the row swizzle repeats every 8
@@ -321,13 +321,16 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     const unsigned hm = sm.khm[e];
     const int t0 = jb * kBlockSize;
     const int tlast = L - 1;   // rows past the sequence are read from its last row and masked
+    const size_t r0 = cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
+    const uint16_t* kb = p.k + r0 * D;   // token t of this block is row t - t0
+    const uint16_t* vb = p.v + r0 * D;
 
     // ---- issue the block's loads: K into registers, V into registers ----
     u32x4_t kr[4][KS];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const int t = min(t0 + 16 * T + h, tlast);
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)t * D + g * (D / 4));
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)(t - t0) * D + g * (D / 4));
 #pragma unroll
       for (int s = 0; s < KS; ++s) kr[T][s] = src[s];
     }
@@ -337,7 +340,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       const int f = n * kWave + lane;        // chunk id within the tile
       const int r = f / VC, q = f % VC;
       const int t = min(t0 + r, tlast);
-      vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)t * D + q * 8));
+      vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)(t - t0) * D + q * 8));
     }
 
     // ---- QK on the matrix cores ----
@@ -462,7 +465,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     return;
   }
   const int nblk = min(p.split_blocks, NB - j0);
-  const size_t bh = (size_t)b * p.Hkv + j;
 
   // ---- prologue: query to LDS, int8 scan query --------------------------
   const uint16_t* qg = p.q + ((size_t)b * p.Hq + (size_t)j * G) * D;
@@ -509,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 
   // ---- scan + select ------------------------------------------------------
   if constexpr (!DENSE) {
-    scan_blocks<D, G>(p, sm, bh, j0, nullptr, sm.blk, nblk, L, lane, w);
+    scan_blocks<D, G>(p, sm, b, j, j0, nullptr, sm.blk, nblk, L, lane, w);
     if (p.pm_sink_local) {
       // the sink and local blocks that lie outside this split are scanned too
       if (tid == 0) {
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
       }
       __syncthreads();
       const int nx = sm.nx;
-      scan_blocks<D, G>(p, sm, bh, 0, sm.xidx, sm.xblk, nx, L, lane, w);
+      scan_blocks<D, G>(p, sm, b, j, 0, sm.xidx, sm.xblk, nx, L, lane, w);
       __syncthreads();
       if (tid < G) {
         float m = -INFINITY;
@@ -543,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 
   // ---- attend -------------------------------------------------------------
   AttendState<D> st;
-  attend_blocks<D, G, DENSE>(p, sm, bh, b, j, j0, L, lane, w, st);
+  attend_blocks<D, G, DENSE>(p, sm, b, j, j0, L, lane, w, st);
 
   // this wave's partial: normaliser of head h summed over its 4 lane groups
   float lw = st.l;

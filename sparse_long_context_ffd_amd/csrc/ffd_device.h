@@ -68,4 +68,18 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+// Row index (in a [rows, D] view of the cache) of token 0 of block jb of
+// sequence b, kv head j. Contiguous cache: [B, Hkv, cap, D]. Paged cache: the
+// block lives in page block_table[b, jb] of a [num_pages, Hkv, 64, D] pool;
+// out-of-range page numbers are clamped so a bad table cannot fault.
+__device__ __forceinline__ size_t cache_block_row(const int32_t* block_table, int table_stride, int num_pages,
+                                                  int cap, int Hkv, int b, int j, int jb) {
+  if (block_table != nullptr) {
+    int pg = block_table[(size_t)b * table_stride + jb];
+    pg = pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg);
+    return ((size_t)pg * Hkv + j) * 64;
+  }
+  return ((size_t)b * Hkv + j) * cap + (size_t)jb * 64;
+}
+
 }  // namespace ffd

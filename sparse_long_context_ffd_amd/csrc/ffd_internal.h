@@ -19,6 +19,8 @@ struct DecodeParams {
   const uint8_t* kq;       // u8   [B, Hkv, cap, D/2]
   const float* kscale;     // f32  [B, Hkv, cap]
   const int32_t* seq_lens; // [B]
+  const int32_t* block_table;  // [B, table_stride] page of each block, or null (contiguous cache)
+  int table_stride, num_pages; // paged cache: K/V [num_pages, Hkv, 64, D], kq/kscale alike
   float* o_part;           // f32  [B, Hq, n_splits, D]   (normalised per split)
   float* lse_part;         // f32  [B, Hq, n_splits]      (natural log)
   uint8_t* mask;           // u8   [B, Hq, nb_max] or null
@@ -44,9 +46,10 @@ inline size_t ws_lse_bytes(int B, int Hq, int n_splits) {
 }
 
 
+// block_table == null: contiguous [B, Hkv, cap, D]; else paged [num_pages, Hkv, 64, D]
 hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, const int32_t* pos_begin,
-                              const int32_t* pos_end, int B, int Hkv, int cap, int D, int max_span,
-                              hipStream_t stream);
+                              const int32_t* pos_end, const int32_t* block_table, int table_stride, int num_pages,
+                              int B, int Hkv, int cap, int D, int max_span, hipStream_t stream);
 
 enum class Stage { kPartials = 1, kCombine = 2, kBoth = 3 };
 

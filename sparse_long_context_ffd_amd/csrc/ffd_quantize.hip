@@ -21,8 +21,9 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
                                                           uint8_t* __restrict__ kq,
                                                           float* __restrict__ kscale,
                                                           const int32_t* __restrict__ pos_begin,
-                                                          const int32_t* __restrict__ pos_end, int Hkv,
-                                                          int cap) {
+                                                          const int32_t* __restrict__ pos_end,
+                                                          const int32_t* __restrict__ block_table, int table_stride,
+                                                          int num_pages, int Hkv, int cap) {
   constexpr int LPT = D / 8;         // lanes per token
   constexpr int TPB = 256 / LPT;     // tokens per workgroup
   const int b = blockIdx.z, j = blockIdx.y;
@@ -31,10 +32,12 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
   int begin = pos_begin[b];
   int end = pos_end[b];
   begin = begin < 0 ? 0 : begin;
-  end = end > cap ? cap : end;
+  const int limit = block_table ? table_stride * 64 : cap;
+  end = end > limit ? limit : end;
   const int t = begin + blockIdx.x * TPB + tid / LPT;
   const bool valid = t < end;
-  const size_t row = ((size_t)b * Hkv + j) * cap + (valid ? t : 0);
+  const int tv = valid ? t : 0;
+  const size_t row = cache_block_row(block_table, table_stride, num_pages, cap, Hkv, b, j, tv / 64) + tv % 64;
 
   uint4 w = make_uint4(0, 0, 0, 0);
   if (valid) w = *reinterpret_cast<const uint4*>(k + row * D + sub * 8);
@@ -69,15 +72,17 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
 }
 
 hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, const int32_t* pos_begin,
-                              const int32_t* pos_end, int B, int Hkv, int cap, int D, int max_span,
-                              hipStream_t stream) {
+                              const int32_t* pos_end, const int32_t* block_table, int table_stride, int num_pages,
+                              int B, int Hkv, int cap, int D, int max_span, hipStream_t stream) {
   const int lpt = D / 8;
   const int tpb = 256 / lpt;
   dim3 grid((max_span + tpb - 1) / tpb, Hkv, B);
   if (D == 128) {
-    quantize_kv_kernel<128><<<grid, 256, 0, stream>>>(k, kq, kscale, pos_begin, pos_end, Hkv, cap);
+    quantize_kv_kernel<128><<<grid, 256, 0, stream>>>(k, kq, kscale, pos_begin, pos_end, block_table, table_stride,
+                                                      num_pages, Hkv, cap);
   } else if (D == 64) {
-    quantize_kv_kernel<64><<<grid, 256, 0, stream>>>(k, kq, kscale, pos_begin, pos_end, Hkv, cap);
+    quantize_kv_kernel<64><<<grid, 256, 0, stream>>>(k, kq, kscale, pos_begin, pos_end, block_table, table_stride,
+                                                     num_pages, Hkv, cap);
   } else {
     return hipErrorInvalidValue;
   }

@@ -32,8 +32,9 @@ FFD_OUT_BF16 = 0
 FFD_OUT_F32 = 1
 PSEUDO_MAX = {"split": 0, "sink_local": 1}
 
-EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_decode_workspace_bytes",
-                    "ffd_decode", "ffd_decode_partials", "ffd_combine")
+EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_quantize_kv_paged",
+                    "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged", "ffd_decode_partials",
+                    "ffd_combine")
 
 
 class FFDError(RuntimeError):
@@ -76,6 +77,14 @@ def lib() -> ctypes.CDLL:
     L.ffd_decode_partials.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                       _i, ctypes.c_float, _i, _i, _i, _i, ctypes.c_float,
                                       _vp, _vp, ctypes.c_size_t, _vp]
+    L.ffd_quantize_kv_paged.restype = _i
+    L.ffd_quantize_kv_paged.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i, _i, _vp]
+    L.ffd_decode_paged.restype = _i
+    L.ffd_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i,      # q kp vp kqp ksp table stride pages
+                                   _vp, _i, _i, _i, _i, _i,                   # seq_lens max_seq_len B Hq Hkv d
+                                   _i, ctypes.c_float, _i, _i, _i, _i,        # block_size delta sink local pm split
+                                   ctypes.c_float, _vp, _i, _vp, _vp,         # sm_scale out out_dtype lse mask
+                                   _vp, ctypes.c_size_t, _vp]                 # workspace bytes stream
     L.ffd_combine.restype = _i
     L.ffd_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _i, _vp, _vp]
     _lib = L
@@ -212,6 +221,55 @@ def ffd_combine(seq_lens, *, max_seq_len: int, block_size: int, split_blocks: in
     odt = _check_outputs(out, lse, B, Hq, d)
     _check(lib().ffd_combine(_ptr(seq_lens), int(max_seq_len), B, Hq, d, int(block_size), int(split_blocks),
                              _ptr(workspace), _ws(workspace), _ptr(out), odt, _ptr(lse), _stream(stream)))
+
+
+def ffd_quantize_kv_paged(k_pages: torch.Tensor, kq_pages: torch.Tensor, kscale_pages: torch.Tensor,
+                          block_table: torch.Tensor, pos_begin: torch.Tensor, pos_end: torch.Tensor, max_span: int,
+                          stream=None) -> None:
+    """Quantise tokens ``[pos_begin[b], pos_end[b])`` of a paged K cache in place."""
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    P, Hkv, bs, d = k_pages.shape
+    if bs != 64:
+        raise ValueError("pages hold 64 tokens")
+    _need(kq_pages, "kq_pages", torch.uint8, 4)
+    _need(kscale_pages, "kscale_pages", torch.float32, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    if tuple(kq_pages.shape) != (P, Hkv, 64, d // 2) or tuple(kscale_pages.shape) != (P, Hkv, 64):
+        raise ValueError("kq/kscale page shapes do not match k_pages")
+    B, stride = block_table.shape
+    _check(lib().ffd_quantize_kv_paged(_ptr(k_pages), _ptr(kq_pages), _ptr(kscale_pages), _ptr(block_table), stride,
+                                       P, _ptr(pos_begin), _ptr(pos_end), B, Hkv, d, int(max_span), _stream(stream)))
+
+
+def ffd_decode_paged(q, k_pages, v_pages, kq_pages, kscale_pages, block_table, seq_lens, *, max_seq_len: int,
+                     block_size: int, delta: float, sink: int, local: int, split_blocks: int, sm_scale: float,
+                     out: torch.Tensor, lse: torch.Tensor, kept_mask: Optional[torch.Tensor],
+                     workspace: Optional[torch.Tensor], pseudo_max: str = "split", stream=None) -> None:
+    """One decode step over a paged cache into preallocated outputs."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    P, Hkv, bs, _ = k_pages.shape
+    if bs != 64 or tuple(k_pages.shape) != (P, Hkv, 64, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k/v pages must be [num_pages, Hkv, 64, d]")
+    _need(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table needs one row per sequence")
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if kq_pages is not None:
+        _need(kq_pages, "kq_pages", torch.uint8, 4)
+        _need(kscale_pages, "kscale_pages", torch.float32, 3)
+    if kept_mask is not None:
+        _need(kept_mask, "kept_mask", torch.uint8, 3)
+        if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
+            raise ValueError("kept_mask shape")
+    odt = _check_outputs(out, lse, B, Hq, d)
+    _check(lib().ffd_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kq_pages), _ptr(kscale_pages),
+                                  _ptr(block_table), block_table.shape[1], P, _ptr(seq_lens), int(max_seq_len), B, Hq,
+                                  Hkv, d, int(block_size), float(delta), int(sink), int(local), _pm(pseudo_max),
+                                  int(split_blocks), float(sm_scale), _ptr(out), odt, _ptr(lse), _ptr(kept_mask),
+                                  _ptr(workspace), _ws(workspace), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -99,3 +99,22 @@ def test_empty_batch_is_a_no_op():
     assert L.ffd_quantize_kv(None, None, None, None, None, 0, 8, 128, 128, 10, None) == ffd.FFD_OK
     assert L.ffd_quantize_kv(None, None, None, None, None, 1, 8, 128, 96, 10, None) == ffd.FFD_ERR_UNSUPPORTED
     assert L.ffd_quantize_kv(None, None, None, None, None, 1, 8, 128, 128, 10, None) == ffd.FFD_ERR_INVALID_ARG
+
+
+def test_paged_validation():
+    L = ffd.lib()
+    f = ctypes.c_float
+    fake = 1 << 20
+    # null block table
+    st = L.ffd_decode_paged(fake, fake, fake, fake, fake, None, 4, 10, fake, 256, 1, 4, 1, 128, 64, f(2.0), 1, 1, 0,
+                            32, f(0.1), fake, 0, fake, None, fake, 1 << 30, None)
+    assert st == ffd.FFD_ERR_INVALID_ARG and "block_table" in ffd.ffd_last_error()
+    # table too narrow for max_seq_len
+    st = L.ffd_decode_paged(fake, fake, fake, fake, fake, fake, 3, 10, fake, 256, 1, 4, 1, 128, 64, f(2.0), 1, 1, 0,
+                            32, f(0.1), fake, 0, fake, None, fake, 1 << 30, None)
+    assert st == ffd.FFD_ERR_INVALID_ARG and "table_stride" in ffd.ffd_last_error()
+    st = L.ffd_decode_paged(fake, fake, fake, fake, fake, fake, 4, 0, fake, 256, 1, 4, 1, 128, 64, f(2.0), 1, 1, 0,
+                            32, f(0.1), fake, 0, fake, None, fake, 1 << 30, None)
+    assert st == ffd.FFD_ERR_INVALID_ARG and "num_pages" in ffd.ffd_last_error()
+    st = L.ffd_quantize_kv_paged(fake, fake, fake, None, 4, 10, fake, fake, 1, 8, 128, 64, None)
+    assert st == ffd.FFD_ERR_INVALID_ARG and "block_table" in ffd.ffd_last_error()

@@ -1,0 +1,114 @@
+"""Paged KV cache: ffd_quantize_kv_paged / ffd_decode_paged over a shuffled
+page pool give bit-identical results to the contiguous entry points on the
+same rows, and match the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_long_context_ffd_amd as ffd
+from ffd_inputs import make_random_inputs
+from oracle import ffd_oracle as O
+from tests.gpu_util import assert_close, assert_mask_equal, say, sm_scale_for, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _paginate(x, lens, table, num_pages, fill):
+    """Scatter a contiguous [B, Hkv, cap, ...] cache into [num_pages, Hkv, 64, ...] pages."""
+    B, Hkv = x.shape[:2]
+    pool = torch.full((num_pages, Hkv, 64) + tuple(x.shape[3:]), fill, dtype=x.dtype, device=x.device)
+    for b in range(B):
+        nb = -(-int(lens[b]) // 64)
+        for j in range(nb):
+            pool[table[b, j]] = x[b, :, 64 * j:64 * j + 64]
+    return pool
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,lens,delta,pm,S", [
+    (3, 16, 4, 128, (5000, 0, 1234), 2.0, "split", 8),
+    (2, 8, 2, 64, (3000, 2999), 1.0, "sink_local", 4),
+    (1, 32, 8, 128, (20000,), 6.0, "split", 32),
+])
+def test_paged_equals_contiguous(B, Hq, Hkv, d, lens, delta, pm, S):
+    say(f"paged B={B} Hq={Hq} Hkv={Hkv} d={d} lens={lens} delta={delta} {pm} S={S}")
+    inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=900 + B, block_size=64)
+    dv = to_device(inp)
+    cap = inp["cap"]
+    nbs = [-(-L // 64) for L in lens]
+    rng = np.random.default_rng(3)
+    num_pages = sum(nbs) + 7
+    perm = rng.permutation(num_pages)
+    stride = cap // 64 + 2
+    table_np = np.full((B, stride), -5, dtype=np.int32)      # unused entries are junk
+    used = 0
+    for b in range(B):
+        table_np[b, :nbs[b]] = perm[used:used + nbs[b]]
+        used += nbs[b]
+    table = torch.from_numpy(table_np).cuda()
+    nan16 = float("nan")
+    k_pages = _paginate(dv["k"], lens, table_np, num_pages, nan16)
+    v_pages = _paginate(dv["v"], lens, table_np, num_pages, nan16)
+    # sketch: paged build vs contiguous build, bit-identical on valid rows
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    kq_pages = torch.full((num_pages, Hkv, 64, d // 2), 0xCD, dtype=torch.uint8, device="cuda")
+    ks_pages = torch.full((num_pages, Hkv, 64), float("nan"), dtype=torch.float32, device="cuda")
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ffd.ffd_quantize_kv_paged(k_pages, kq_pages, ks_pages, table, zeros, dv["seq_lens"], cap)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for j in range(nbs[b]):
+            n = min(64, lens[b] - 64 * j)
+            pg = table_np[b, j]
+            assert torch.equal(kq_pages[pg, :, :n], kq[b, :, 64 * j:64 * j + n])
+            assert torch.equal(ks_pages[pg, :, :n].view(torch.int32), ks[b, :, 64 * j:64 * j + n].view(torch.int32))
+    sm = sm_scale_for(d)
+    kw = dict(max_seq_len=cap, block_size=64, delta=delta, sink=1, local=2, split_blocks=S, sm_scale=sm,
+              pseudo_max=pm)
+    outs = []
+    for paged in (False, True):
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        mask = torch.empty((B, Hq, cap // 64), dtype=torch.uint8, device="cuda")
+        ws = ffd.alloc_workspace(B, Hq, d, cap, 64, S)
+        if paged:
+            ffd.ffd_decode_paged(dv["q"], k_pages, v_pages, kq_pages, ks_pages, table, dv["seq_lens"], out=out,
+                                 lse=lse, kept_mask=mask, workspace=ws, **kw)
+        else:
+            ffd.ffd_decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], out=out, lse=lse, kept_mask=mask,
+                           workspace=ws, **kw)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), lse.cpu().numpy(), mask.cpu().numpy()))
+    for a, b_ in zip(outs[0], outs[1]):
+        np.testing.assert_array_equal(a, b_)
+    r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=cap, block_size=64,
+                                    delta=delta, sink=1, local=2, split_blocks=S, sm_scale=np.float32(sm),
+                                    pseudo_max=pm)
+    assert_mask_equal(outs[1][2], r_mask, "paged mask")
+    assert_close(outs[1][0], r_out, "paged out")
+    assert_close(outs[1][1], r_lse, "paged lse")
+
+
+def test_paged_dense_path():
+    say("paged dense (delta = inf)")
+    inp = make_random_inputs(2, 8, 2, 128, (700, 129), seed=5, block_size=64)
+    dv = to_device(inp)
+    lens = (700, 129)
+    # 11 + 3 blocks on 14 distinct pages; junk past each sequence's blocks
+    table_np = np.array([[3, 0, 5, 7, 1, 2, 4, 6, 13, 9, 12, -7], [10, 8, 11, 99, -1, -1, -1, -1, -1, -1, -1, -1]],
+                        dtype=np.int32)
+    table = torch.from_numpy(table_np).cuda()
+    k_pages = _paginate(dv["k"], lens, table_np, 14, float("nan"))
+    v_pages = _paginate(dv["v"], lens, table_np, 14, float("nan"))
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((2, 8), dtype=torch.float32, device="cuda")
+    ws = ffd.alloc_workspace(2, 8, 128, inp["cap"], 64, 4)
+    ffd.ffd_decode_paged(dv["q"], k_pages, v_pages, None, None, table, dv["seq_lens"], max_seq_len=inp["cap"],
+                         block_size=64, delta=float("inf"), sink=0, local=0, split_blocks=4,
+                         sm_scale=sm_scale_for(128), out=out, lse=lse, kept_mask=None, workspace=ws)
+    torch.cuda.synchronize()
+    r_out, r_lse, _ = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"], block_size=64,
+                               delta=float("inf"), sink=0, local=0, split_blocks=4, sm_scale=np.float32(sm_scale_for(128)),
+                               quantize=False)
+    assert_close(out.cpu().numpy(), r_out, "paged dense out")
+    assert_close(lse.cpu().numpy(), r_lse, "paged dense lse")
