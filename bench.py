@@ -135,6 +135,8 @@ def main() -> int:
     ap.add_argument("--delta", type=float, default=None, help="default: the workload's first delta")
     ap.add_argument("--pseudo-max", default="split", choices=["split", "sink_local"],
                     help="split-local max (default) or the sink/local estimate")
+    ap.add_argument("--paged", action="store_true",
+                    help="keep the cache in a shuffled page pool and call ffd_decode_paged's kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the delta=inf comparison")
@@ -206,9 +208,42 @@ def main() -> int:
     ws = ffd.alloc_workspace(B, w.Hq, d, msl, w.block_size, w.split_blocks, dev)
     kw = dict(max_seq_len=msl, block_size=w.block_size, split_blocks=w.split_blocks)
 
+    if args.paged:
+        # same rows in a shuffled pool of 64-token pages; the block table maps them
+        nbs = [-(-int(L) // w.block_size) for L in inp["seq_lens"]]
+        stride = msl // w.block_size
+        num_pages = sum(nbs)
+        perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(0)).to(torch.int32)
+        table = torch.zeros((B, stride), dtype=torch.int32)
+        kp = torch.empty((num_pages, Hkv, 64, d), dtype=torch.bfloat16, device=dev)
+        vp = torch.empty_like(kp)
+        kqp = torch.empty((num_pages, Hkv, 64, d // 2), dtype=torch.uint8, device=dev)
+        ksp = torch.empty((num_pages, Hkv, 64), dtype=torch.float32, device=dev)
+        used = 0
+        for b in range(B):
+            nb = nbs[b]
+            table[b, :nb] = perm[used:used + nb]
+            used += nb
+            pages = table[b, :nb].to(dev, torch.int64)
+            for src, dst in ((k, kp), (v, vp), (kq, kqp), (ks, ksp)):
+                blk = src[b, :, :64 * nb].reshape((Hkv, nb, 64) + tuple(src.shape[3:]))
+                dst[pages] = blk.transpose(0, 1)
+        table = table.to(dev)
+        del k, v, kq, ks
+        torch.cuda.synchronize()
+
     def step(dl, ev=None):
         if ev is not None:
             ev[0].record()
+        if args.paged:
+            # the two launches of ffd_decode_paged, with an event between them
+            ffd.ffd_decode_paged(q, kp, vp, None if math.isinf(dl) else kqp, None if math.isinf(dl) else ksp,
+                                 table, seq, delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale, out=out,
+                                 lse=lse, kept_mask=mask, workspace=ws, pseudo_max=args.pseudo_max, **kw)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
         ffd.ffd_decode_partials(q, k, v, None if math.isinf(dl) else kq, None if math.isinf(dl) else ks, seq,
                                 delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale, kept_mask=mask,
                                 workspace=ws, pseudo_max=args.pseudo_max, **kw)
@@ -261,10 +296,12 @@ def main() -> int:
             "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "block_size": w.block_size,
             "delta": None if dense else delta, "sink_blocks": w.sink, "local_blocks": w.local,
             "split_blocks": w.split_blocks, "pseudo_max": args.pseudo_max, "out_dtype": "f32",
+            "kv_layout": "paged (64-token pages, shuffled)" if args.paged else "contiguous",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)",
+            "kernel": ("fused_decode_kernel + combine_kernel (ffd_decode_paged)" if args.paged else
+                       "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -65,6 +65,7 @@ struct DecodeSmem {
   float xblk[kMaxPseudoMax][G];
   float pm[G];              // sink/local pseudo-max per head
   float seed[G];            // split max of the block scores (natural-log units)
+  int rowp[kMaxSplit];      // paged cache: first cache row of each block of the split
   uint8_t kidx[kMaxSplit];  // kept blocks (split-local index)
   uint8_t khm[kMaxSplit];   // per-head keep bits of each kept block
   int nkept;
@@ -77,6 +78,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// First cache row of block jb of (sequence b, kv head j). For a paged cache
+// the split's rows were looked up once into LDS (rowp); blocks outside the
+// split (sink/local pseudo-max) read the block table directly.
+template <int D, int G>
+__device__ __forceinline__ size_t block_row(const DecodeParams& p, const DecodeSmem<D, G>& sm, int b, int j, int j0,
+                                            int nblk, int jb) {
+  if (p.block_table != nullptr && jb >= j0 && jb < j0 + nblk) return (size_t)(unsigned)sm.rowp[jb - j0] * kBlockSize;
+  return cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
+}
 
 __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) {
   return (int)((uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
@@ -91,8 +102,8 @@ template <int D, int G>
 // Scores of `nblk` blocks: block j0 + i, or xlist[i] when xlist is given,
 // written to out[i][h].
 __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
-                                            const int* xlist, float (*out)[G], int nblk, int L, int lane,
-                                            int w) {
+                                            int nblk_split, const int* xlist, float (*out)[G], int nblk, int L,
+                                            int lane, int w) {
   constexpr int NCW = D / 32;  // 32-bit code words per lane (8 codes each)
   const int quad = lane >> 2;
   const int ql = lane & 3;
@@ -127,7 +138,7 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
       if (jl < nblk) {
         const int jb = xlist ? xlist[jl] : j0 + jl;
         const int t0 = jb * kBlockSize;
-        const size_t r0 = cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
+        const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
         const uint8_t* kq = p.kq + r0 * (D / 2);
         const float* ks = p.kscale + r0;
 #pragma unroll
@@ -321,7 +332,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     const unsigned hm = sm.khm[e];
     const int t0 = jb * kBlockSize;
     const int tlast = L - 1;   // rows past the sequence are read from its last row and masked
-    const size_t r0 = cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
+    const size_t r0 = block_row(p, sm, b, j, j0, kMaxSplit, jb);   // kept blocks lie in the split
     const uint16_t* kb = p.k + r0 * D;   // token t of this block is row t - t0
     const uint16_t* vb = p.v + r0 * D;
 
@@ -469,6 +480,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   // ---- prologue: query to LDS, int8 scan query --------------------------
   const uint16_t* qg = p.q + ((size_t)b * p.Hq + (size_t)j * G) * D;
   for (int i = tid; i < G * D; i += kThreads) sm.q[i / D][i % D] = bf16_to_f32(qg[i]);
+  if (p.block_table != nullptr && tid < nblk)
+    sm.rowp[tid] = (int)(cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, j0 + tid) /
+                         kBlockSize);
   __syncthreads();
   const float qscale = p.sm_scale * kLog2e;
   for (int h = w; h < G; h += kWaves) {
@@ -511,7 +525,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 
   // ---- scan + select ------------------------------------------------------
   if constexpr (!DENSE) {
-    scan_blocks<D, G>(p, sm, b, j, j0, nullptr, sm.blk, nblk, L, lane, w);
+    scan_blocks<D, G>(p, sm, b, j, j0, nblk, nullptr, sm.blk, nblk, L, lane, w);
     if (p.pm_sink_local) {
       // the sink and local blocks that lie outside this split are scanned too
       if (tid == 0) {
@@ -526,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
       }
       __syncthreads();
       const int nx = sm.nx;
-      scan_blocks<D, G>(p, sm, b, j, 0, sm.xidx, sm.xblk, nx, L, lane, w);
+      scan_blocks<D, G>(p, sm, b, j, j0, nblk, sm.xidx, sm.xblk, nx, L, lane, w);
       __syncthreads();
       if (tid < G) {
         float m = -INFINITY;
