@@ -99,11 +99,11 @@ __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) 
 // Selection": stream the low-bit keys, compute tentative scores per block)
 // ---------------------------------------------------------------------------
 template <int D, int G>
-// Scores of `nblk` blocks: block j0 + i, or xlist[i] when xlist is given,
-// written to out[i][h].
+// Scores of the split's nblk_split blocks (block j0 + i -> sm.blk[i]) followed
+// by nx extra blocks (sm.xidx[x] -> sm.xblk[x]), in one pass.
 __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
-                                            int nblk_split, const int* xlist, float (*out)[G], int nblk, int L,
-                                            int lane, int w) {
+                                            int nblk_split, int nx, int L, int lane, int w) {
+  const int nblk = nblk_split + nx;
   constexpr int NCW = D / 32;  // 32-bit code words per lane (8 codes each)
   const int quad = lane >> 2;
   const int ql = lane & 3;
@@ -136,7 +136,7 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
       if (jl < nblk) {
-        const int jb = xlist ? xlist[jl] : j0 + jl;
+        const int jb = jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split];
         const int t0 = jb * kBlockSize;
         const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
         const uint8_t* kq = p.kq + r0 * (D / 2);
@@ -160,7 +160,7 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
       if (jl >= nblk) continue;
-      const int t0 = (xlist ? xlist[jl] : j0 + jl) * kBlockSize;
+      const int t0 = (jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split]) * kBlockSize;
       float bm[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
@@ -201,7 +201,10 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
       }
       if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) out[jl][h] = bm[h];
+        for (int h = 0; h < G; ++h) {
+          if (jl < nblk_split) sm.blk[jl][h] = bm[h];
+          else sm.xblk[jl - nblk_split][h] = bm[h];
+        }
       }
     }
   }
@@ -483,6 +486,16 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   if (p.block_table != nullptr && tid < nblk)
     sm.rowp[tid] = (int)(cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, j0 + tid) /
                          kBlockSize);
+  if (!DENSE && p.pm_sink_local && tid == 0) {
+    int nx = 0;
+    const int s_end = min(p.sink, NB);
+    const int l_beg = max(s_end, NB - p.local);
+    for (int jb = 0; jb < s_end; ++jb)
+      if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
+    for (int jb = l_beg; jb < NB; ++jb)
+      if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
+    sm.nx = nx;
+  }
   __syncthreads();
   const float qscale = p.sm_scale * kLog2e;
   for (int h = w; h < G; h += kWaves) {
@@ -525,34 +538,21 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 
   // ---- scan + select ------------------------------------------------------
   if constexpr (!DENSE) {
-    scan_blocks<D, G>(p, sm, b, j, j0, nblk, nullptr, sm.blk, nblk, L, lane, w);
-    if (p.pm_sink_local) {
-      // the sink and local blocks that lie outside this split are scanned too
-      if (tid == 0) {
-        int nx = 0;
-        const int s_end = min(p.sink, NB);
-        const int l_beg = max(s_end, NB - p.local);
-        for (int jb = 0; jb < s_end; ++jb)
-          if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
-        for (int jb = l_beg; jb < NB; ++jb)
-          if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
-        sm.nx = nx;
-      }
-      __syncthreads();
-      const int nx = sm.nx;
-      scan_blocks<D, G>(p, sm, b, j, j0, nblk, sm.xidx, sm.xblk, nx, L, lane, w);
-      __syncthreads();
-      if (tid < G) {
-        float m = -INFINITY;
-        for (int x = 0; x < nx; ++x) m = fmaxf(m, sm.xblk[x][tid]);
-        for (int jl = 0; jl < nblk; ++jl) {
-          const int jb = j0 + jl;
-          if (jb < p.sink || jb >= NB - p.local) m = fmaxf(m, sm.blk[jl][tid]);
-        }
-        sm.pm[tid] = m;
-      }
-    }
+    // sink/local pseudo-max: the sink and local blocks outside this split are
+    // listed in the prologue and scanned in the same pass as the split
+    const int nx = p.pm_sink_local ? sm.nx : 0;
+    scan_blocks<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
     __syncthreads();
+    if (p.pm_sink_local && tid < G) {
+      float m = -INFINITY;
+      for (int x = 0; x < nx; ++x) m = fmaxf(m, sm.xblk[x][tid]);
+      for (int jl = 0; jl < nblk; ++jl) {
+        const int jb = j0 + jl;
+        if (jb < p.sink || jb >= NB - p.local) m = fmaxf(m, sm.blk[jl][tid]);
+      }
+      sm.pm[tid] = m;
+    }
+    if (p.pm_sink_local) __syncthreads();
   }
   if (w == 0) select_blocks<D, G, DENSE>(p, sm, b, j, j0, nblk, nmask, NB, lane);
   __syncthreads();
