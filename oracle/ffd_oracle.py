@@ -42,6 +42,20 @@ choice of this library, applied identically by the HIP path):
 * The kept blocks are attended exactly ([TS] Methodology 3, "Fine-Grained
   Refinement"); here that is done in fp64.
 
+Second storage scheme ("thumb"), closer to the pages' own ([TS] Methodology
+1: 2-bit key thumbnails for the scan, 8-bit residuals that reconstruct the keys
+for refinement). The formats are not given there; this library fixes them:
+
+* thumbnail: t = fl32(amax/3); x = fl32(k * fl32(3/amax));
+  u = clamp(rne(fl32(fl32(x + 3) * 0.5)), 0, 3); level (2u - 3) * t, i.e. one
+  of {-3t, -t, t, 3t};
+* residual: r = fl32(k - fl32((2u - 3) * t)), quantised to int8 with its own
+  per-token scale exactly like the int8 query (amax/127, clamp to +-127);
+* reconstructed key K^ = (2u - 3) * t + s8 * r8 in exact arithmetic; the
+  refinement attends over K^ (fp64 here), V stays bf16;
+* the scan uses the thumbnail: dot = sum qc * (2u - 3) (exact integer),
+  s^ = fl32(float(dot) * fl32(t * cq)).
+
 Floating point: every selection step is done in explicit np.float32 scalars
 and arrays (no Python floats, which would promote to fp64), so the kept-block
 mask is reproducible bit for bit. Attention is done in fp64.
@@ -60,6 +74,8 @@ QUERY_QMAX = 127  # int8 symmetric range
 # smaller amax, fl32(QMAX / amax) would overflow to +inf (and 0 * inf = NaN).
 KEY_TINY = np.float32(2.0 ** -125)
 QUERY_TINY = np.float32(2.0 ** -120)
+THUMB_QMAX = 3   # thumbnail levels (2u - 3) in {-3, -1, 1, 3}
+RESID_QMAX = 127
 
 
 # --------------------------------------------------------------------------
@@ -113,6 +129,88 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     out[..., 0::2] = lo
     out[..., 1::2] = hi
     return out
+
+
+# --------------------------------------------------------------------------
+# O1': thumbnail + residual keys ("thumb" storage)    [TS] Methodology 1, 3
+# --------------------------------------------------------------------------
+
+def quantize_keys_thumb(k32: np.ndarray):
+    """2-bit thumbnail codes and an int8 residual per key row ``[..., d]``.
+
+    Returns ``(u uint8 [..., d] in 0..3, t float32 [...], r8 int8 [..., d],
+    s8 float32 [...])``. A row with amax < 2^-125 gives t = 0, u = 0, r8 = 0,
+    s8 = 0 (reconstructs to zero); a residual with amax < 2^-120 gives s8 = 0,
+    r8 = 0."""
+    k32 = np.asarray(k32, dtype=np.float32)
+    amax = np.max(np.abs(k32), axis=-1)
+    nz = amax >= KEY_TINY
+    safe = np.where(nz, amax, F32(1)).astype(np.float32)
+    inv = (F32(THUMB_QMAX) / safe).astype(np.float32)
+    t = np.where(nz, (safe / F32(THUMB_QMAX)).astype(np.float32), F32(0)).astype(np.float32)
+    x = (k32 * inv[..., None]).astype(np.float32)
+    y = ((x + F32(3)).astype(np.float32) * F32(0.5)).astype(np.float32)
+    u = np.clip(np.rint(y), 0, 3).astype(np.int64)
+    u[~nz] = 0
+    lev = ((2 * u - 3).astype(np.float32) * t[..., None]).astype(np.float32)
+    r = (k32 - lev).astype(np.float32)
+    r[~nz] = 0
+    ar = np.max(np.abs(r), axis=-1)
+    nzr = ar >= QUERY_TINY
+    safe_r = np.where(nzr, ar, F32(1)).astype(np.float32)
+    inv_r = (F32(RESID_QMAX) / safe_r).astype(np.float32)
+    s8 = np.where(nzr, (safe_r / F32(RESID_QMAX)).astype(np.float32), F32(0)).astype(np.float32)
+    r8 = np.clip(np.rint((r * inv_r[..., None]).astype(np.float32)), -RESID_QMAX, RESID_QMAX).astype(np.int8)
+    r8[~nzr] = 0
+    return u.astype(np.uint8), t, r8, s8
+
+
+def reconstruct_thumb(u: np.ndarray, t: np.ndarray, r8: np.ndarray, s8: np.ndarray) -> np.ndarray:
+    """K^ = (2u - 3) * t + s8 * r8, exact in fp64."""
+    return ((2 * u.astype(np.float64) - 3) * t.astype(np.float64)[..., None]
+            + s8.astype(np.float64)[..., None] * r8.astype(np.float64))
+
+
+def pack_2bit(u: np.ndarray) -> np.ndarray:
+    """Four 2-bit codes per byte: element 4i + c in bits 2c..2c+1 of byte i."""
+    u = np.asarray(u, dtype=np.uint8) & np.uint8(3)
+    return (u[..., 0::4] | (u[..., 1::4] << np.uint8(2)) | (u[..., 2::4] << np.uint8(4))
+            | (u[..., 3::4] << np.uint8(6))).astype(np.uint8)
+
+
+def unpack_2bit(packed: np.ndarray) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (4 * p.shape[-1],), dtype=np.uint8)
+    for c in range(4):
+        out[..., c::4] = (p >> np.uint8(2 * c)) & np.uint8(3)
+    return out
+
+
+def thumb_token_scores(qc: np.ndarray, cq, u: np.ndarray, t: np.ndarray) -> np.ndarray:
+    """s^_t = fl32(float32(dot_t) * fl32(t_t * cq)), dot_t = sum qc * (2u - 3)."""
+    dot = (2 * u.astype(np.int64) - 3) @ np.asarray(qc, dtype=np.int64)
+    w = (np.asarray(t, dtype=np.float32) * F32(cq)).astype(np.float32)
+    return (dot.astype(np.float32) * w).astype(np.float32)
+
+
+def quantize_cache_thumb(k, seq_lens):
+    """Thumbnail cache of a bf16 K cache ``[B, Hkv, cap, d]``: ``(k2 uint8
+    [B,Hkv,cap,d/4], t f32 [B,Hkv,cap], kr int8 [B,Hkv,cap,d], s8 f32
+    [B,Hkv,cap])``; rows at or past a sequence's length are left 0."""
+    B, Hkv, cap, d = k.shape
+    k2 = np.zeros((B, Hkv, cap, d // 4), dtype=np.uint8)
+    t = np.zeros((B, Hkv, cap), dtype=np.float32)
+    kr = np.zeros((B, Hkv, cap, d), dtype=np.int8)
+    s8 = np.zeros((B, Hkv, cap), dtype=np.float32)
+    for b in range(B):
+        L = max(0, min(int(seq_lens[b]), cap))
+        for j in range(Hkv):
+            u, tt, r8, ss = quantize_keys_thumb(bf16_bits_to_f32(k[b, j, :L]))
+            k2[b, j, :L] = pack_2bit(u)
+            t[b, j, :L] = tt
+            kr[b, j, :L] = r8
+            s8[b, j, :L] = ss
+    return k2, t, kr, s8
 
 
 # --------------------------------------------------------------------------
@@ -221,12 +319,15 @@ def attend(q64: np.ndarray, k64: np.ndarray, v64: np.ndarray, sm_scale) -> tuple
 
 def select_head(q32: np.ndarray, codes: np.ndarray, scale: np.ndarray, k64: np.ndarray, L: int,
                 block_size: int, delta, sink: int, local: int, split_blocks: int, sm_scale,
-                quantize: bool = True, pseudo_max: str = "split") -> np.ndarray:
+                quantize: bool = True, pseudo_max: str = "split", thumb=None) -> np.ndarray:
     """Kept-block mask of one query head over one sequence (O2-O6).
 
     With ``quantize=False`` the tentative scores are replaced by the exact fp64
     logits and the threshold is taken in fp64 (used to check the dense limit)."""
-    if quantize:
+    if thumb is not None:
+        qc, cq = quantize_query(q32, sm_scale)
+        tok = thumb_token_scores(qc, cq, thumb[0][:L], thumb[1][:L])
+    elif quantize:
         qc, cq = quantize_query(q32, sm_scale)
         tok = token_scores(qc, cq, codes[:L], scale[:L])
     else:
@@ -237,7 +338,7 @@ def select_head(q32: np.ndarray, codes: np.ndarray, scale: np.ndarray, k64: np.n
 
 def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink: int, local: int,
            split_blocks: int, sm_scale=None, quantize: bool = True, heads=None, mask_only: bool = False,
-           pseudo_max: str = "split"):
+           pseudo_max: str = "split", storage: str = "int4"):
     """One FFD decode step.
 
     ``q`` bf16 bits ``[B, Hq, d]``; ``k``, ``v`` bf16 bits ``[B, Hkv, cap, d]``;
@@ -250,7 +351,12 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
     the work to a list of ``(b, h)`` pairs (other rows are left NaN / 0);
     ``mask_only`` skips the attention step (out and lse stay NaN).
     ``pseudo_max`` picks how m~ is estimated (see :func:`select_blocks`).
+    ``storage="thumb"`` scans 2-bit thumbnails and attends over the
+    reconstructed keys K^ (see :func:`quantize_keys_thumb`) instead of the int4
+    sketch and the bf16 keys.
     """
+    if storage not in ("int4", "thumb"):
+        raise ValueError("storage must be 'int4' or 'thumb'")
     q = np.asarray(q)
     B, Hq, d = q.shape
     Hkv = k.shape[1]
@@ -276,13 +382,18 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
                     lse[b, h] = -math.inf
                 continue
             k32 = bf16_bits_to_f32(k[b, j, :L])
-            k64 = k32.astype(np.float64) if (not mask_only or not quantize) else None
+            thumb = None
+            if storage == "thumb":
+                thumb = quantize_keys_thumb(k32)
+                k64 = None if mask_only else reconstruct_thumb(*thumb)
+            else:
+                k64 = k32.astype(np.float64) if (not mask_only or not quantize) else None
             v64 = None if mask_only else bf16_bits_to_f32(v[b, j, :L]).astype(np.float64)
-            codes, scale = quantize_keys(k32) if quantize else (None, None)
+            codes, scale = quantize_keys(k32) if (quantize and storage == "int4") else (None, None)
             for h in hs:
                 q32 = bf16_bits_to_f32(q[b, h])
                 keep = select_head(q32, codes, scale, k64, L, block_size, delta, sink, local,
-                                   split_blocks, sm_scale, quantize, pseudo_max)
+                                   split_blocks, sm_scale, quantize, pseudo_max, thumb)
                 mask[b, h, :keep.shape[0]] = keep
                 if mask_only:
                     continue
