@@ -104,6 +104,29 @@ ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* 
                                  const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int d,
                                  int max_span, void* stream);
 
+/*
+ * ffd_quantize_kv_thumb -- the pages' own key storage ([TS] Methodology 1: a
+ * 2-bit "thumbnail" of every key for the scan plus an 8-bit residual that
+ * reconstructs the key for the refinement). The formats are this library's:
+ * per token and kv head, with k = K[b, j, t, :] and amax = max|k_i|:
+ *   t = fl32(amax / 3); x_i = fl32(k_i * fl32(3 / amax));
+ *   u_i = clamp(round_half_even(fl32(fl32(x_i + 3) * 0.5)), 0, 3)
+ *     (2-bit code; the level is (2u - 3) * t, one of -3t, -t, t, 3t)
+ *   r_i = fl32(k_i - fl32((2u_i - 3) * t)); s8 = fl32(amax_r / 127);
+ *   r8_i = clamp(round_half_even(fl32(r_i * fl32(127 / amax_r))), -127, 127)
+ *   (amax < 2^-125: t = 0, u = r8 = 0, s8 = 0; amax_r < 2^-120: s8 = 0, r8 = 0)
+ * and the reconstructed key is K^ = (2u - 3) t + s8 r8.
+ *   k        bf16 [B, Hkv, cap, d]     input
+ *   k2       uint8 [B, Hkv, cap, d/4]  codes, element 4i + c in bits 2c of byte i
+ *   k2scale  f32 [B, Hkv, cap]         t
+ *   kr       int8 [B, Hkv, cap, d]     r8
+ *   krscale  f32 [B, Hkv, cap]         s8
+ * Other arguments and conventions as ffd_quantize_kv. d in {64, 128}.
+ */
+ffd_status ffd_quantize_kv_thumb(const void* k, uint8_t* k2, float* k2scale, int8_t* kr, float* krscale,
+                                 const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int cap, int d,
+                                 int max_span, void* stream);
+
 /* Bytes of scratch that ffd_decode, ffd_decode_partials and ffd_combine need
  * for these sizes: per-split partial outputs and log-sum-exps (fp32). 0 for
  * unsupported sizes. */
@@ -193,6 +216,22 @@ ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pa
                             int block_size, float delta, int sink_blocks, int local_blocks,
                             int pseudo_max, int split_blocks, float sm_scale,
                             void* out, int out_dtype, float* lse, uint8_t* kept_mask,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ffd_decode_thumb -- ffd_decode over the thumbnail + residual key storage of
+ * ffd_quantize_kv_thumb (no bf16 K is read). The scan uses the thumbnail:
+ * dot = sum qc_i (2u_i - 3) (exact integer), score fl32(float(dot) *
+ * fl32(t * cq)); selection as in ffd_decode; the refinement is exact softmax
+ * attention over the reconstructed keys, logit sm_scale * q.K^ with K^ =
+ * (2u - 3) t + s8 r8, and the bf16 V. Same outputs, workspace and errors as
+ * ffd_decode (kq/kscale/k replaced by k2, k2scale, kr, krscale).
+ */
+ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2scale, const int8_t* kr,
+                            const float* krscale, const void* v, const int32_t* seq_lens, int max_seq_len,
+                            int B, int Hq, int Hkv, int d, int cap, int block_size, float delta,
+                            int sink_blocks, int local_blocks, int pseudo_max, int split_blocks,
+                            float sm_scale, void* out, int out_dtype, float* lse, uint8_t* kept_mask,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -22,10 +22,13 @@ from .ffd import (  # noqa: F401
     ffd_decode,
     ffd_decode_paged,
     ffd_decode_partials,
+    ffd_decode_thumb,
     ffd_decode_workspace_bytes,
     ffd_last_error,
     ffd_quantize_kv,
     ffd_quantize_kv_paged,
+    ffd_quantize_kv_thumb,
     lib,
     quantize_kv,
+    quantize_kv_thumb,
 )

@@ -76,6 +76,26 @@ ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale, const int3
                          max_span, stream);
 }
 
+ffd_status ffd_quantize_kv_thumb(const void* k, uint8_t* k2, float* k2scale, int8_t* kr, float* krscale,
+                                 const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int cap, int d,
+                                 int max_span, void* stream) {
+  const char* fn = "ffd_quantize_kv_thumb";
+  if (B < 0 || Hkv < 0 || cap < 0 || max_span < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: negative size (B=%d Hkv=%d cap=%d max_span=%d)", fn, B, Hkv, cap, max_span);
+  if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
+  if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
+  if (B == 0 || Hkv == 0 || cap == 0 || max_span == 0) return ok();
+  if (!k || !k2 || !k2scale || !kr || !krscale || !pos_begin || !pos_end)
+    return fail(FFD_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned16(k) || !aligned16(k2) || !aligned16(kr))
+    return fail(FFD_ERR_INVALID_ARG, "%s: k, k2, kr must be 16-byte aligned", fn);
+  if (B > 65535 || Hkv > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B and Hkv must be <= 65535", fn);
+  hipError_t e = ffd::launch_quantize_thumb(static_cast<const uint16_t*>(k), k2, k2scale, kr, krscale, pos_begin,
+                                            pos_end, B, Hkv, cap, d, max_span, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FFD_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
 ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* kscale_pages,
                                  const int32_t* block_table, int table_stride, int num_pages,
                                  const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int d,
@@ -264,6 +284,44 @@ ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pa
   p.lse = lse;
   p.out_f32 = out_dtype == FFD_OUT_F32;
   return launch(fn, p, d, G, dense, ffd::Stage::kBoth, stream);
+}
+
+ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2scale, const int8_t* kr,
+                            const float* krscale, const void* v, const int32_t* seq_lens, int max_seq_len, int B,
+                            int Hq, int Hkv, int d, int cap, int block_size, float delta, int sink_blocks,
+                            int local_blocks, int pseudo_max, int split_blocks, float sm_scale, void* out,
+                            int out_dtype, float* lse, uint8_t* kept_mask, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const char* fn = "ffd_decode_thumb";
+  ffd::DecodeParams p;
+  int G;
+  bool dense;
+  ffd_status st = check_out_dtype(fn, out_dtype);
+  if (st != FFD_OK) return st;
+  if (B > 0 && max_seq_len > 0 && (!k2 || !k2scale || !kr || !krscale))
+    return fail(FFD_ERR_INVALID_ARG, "%s: null thumbnail/residual pointer", fn);
+  if (!aligned16(k2) || !aligned16(kr)) return fail(FFD_ERR_INVALID_ARG, "%s: k2 and kr must be 16-byte aligned", fn);
+  // the thumbnail codes stand in for the int4 sketch and K in the shared checks
+  st = prepare_decode(fn, q, v, v, k2, k2scale, seq_lens, max_seq_len, B, Hq, Hkv, d, cap, block_size, delta,
+                      sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, workspace,
+                      workspace_bytes, nullptr, 0, 0, p, G, dense);
+  if (st != FFD_OK) return st;
+  st = check_out_ptrs(fn, B, out, lse);
+  if (st != FFD_OK) return st;
+  p.k = nullptr;
+  p.kq = nullptr;
+  p.kscale = nullptr;
+  p.k2 = k2;
+  p.k2scale = k2scale;
+  p.kr = kr;
+  p.krscale = krscale;
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = out_dtype == FFD_OUT_F32;
+  if (p.B == 0) return ok();
+  hipError_t e = ffd::launch_decode(p, d, G, dense, ffd::Stage::kBoth, static_cast<hipStream_t>(stream), true);
+  if (e != hipSuccess) return fail(FFD_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
 }
 
 ffd_status ffd_decode_partials(const void* q, const void* k, const void* v, const uint8_t* kq,

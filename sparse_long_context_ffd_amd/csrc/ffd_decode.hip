@@ -59,6 +59,7 @@ struct DecodeSmem {
   int8_t qc[G][D];          // int8 scan query
   float cq[G];              // fl32(sq * sm_scale)
   int sumq[G];              // sum of qc (offset-binary correction)
+  float qsumf[G];           // sum of the bf16 query (thumbnail refinement correction)
   float blk[kMaxSplit][G];  // block scores of the split
   int xidx[kMaxPseudoMax];  // sink/local blocks outside the split (sink/local pseudo-max)
   int nx;
@@ -78,6 +79,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // First cache row of block jb of (sequence b, kv head j). For a paged cache
 // the split's rows were looked up once into LDS (rowp); blocks outside the
@@ -210,6 +212,113 @@ __device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D,
   }
 }
 
+// Thumbnail scan: the same block scores from 2-bit codes u ([TS] Methodology
+// 1: the thumbnails are what the scan streams). dot = 2 * sum qc*u - 3 * sum qc
+// (exact integer); s^ = fl32(float(dot) * fl32(t * cq)). A quad of lanes owns a
+// token; each lane D/64 code words (16 codes each); byte m of
+// (word >> 2k) & 0x03030303 is code 4m + k, matched by a permuted query.
+template <int D, int G>
+__device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j,
+                                                  int j0, int nblk_split, int nx, int L, int lane, int w) {
+  constexpr int NW = D / 64;   // code words per lane
+  const int nblk = nblk_split + nx;
+  const int quad = lane >> 2;
+  const int ql = lane & 3;
+  int qp[G][NW][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int i = 0; i < NW; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int8_t* s = &sm.qc[h][ql * (D / 4) + 16 * i + k];
+        qp[h][i][k] = pack4_i8(s[0], s[4], s[8], s[12]);
+      }
+  int corr[G];
+  float cq[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    corr[h] = 3 * sm.sumq[h];
+    cq[h] = sm.cq[h];
+  }
+  constexpr int kChunk = 4;
+  for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
+    uint32_t cw[kChunk][4][NW];
+    float sc[kChunk][4];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int jl = jc + c * kWaves;
+      if (jl < nblk) {
+        const int jb = jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split];
+        const int t0 = jb * kBlockSize;
+        const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
+        const uint8_t* k2 = p.k2 + r0 * (D / 4);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int t = t0 + it * 16 + quad;
+          const bool ok = t < L;
+          const uint8_t* src = k2 + (size_t)(ok ? t - t0 : 0) * (D / 4) + ql * (D / 16);
+          if constexpr (NW == 2) {
+            const u32x2_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{0u, 0u};
+            cw[c][it][0] = u.x;
+            cw[c][it][1] = u.y;
+          } else {
+            cw[c][it][0] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src)) : 0u;
+          }
+          sc[c][it] = ok ? __builtin_nontemporal_load(p.k2scale + r0 + (t - t0)) : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int jl = jc + c * kWaves;
+      if (jl >= nblk) continue;
+      const int t0 = (jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split]) * kBlockSize;
+      float bm[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        int acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int bytes = (int)((cw[c][it][i] >> (2 * k)) & 0x03030303u);
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h] = __builtin_amdgcn_sdot4(bytes, qp[h][i][k], acc[h], false);
+          }
+        const bool ok = t0 + it * 16 + quad < L;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const int dot = 2 * quad_sum_i(acc[h]) - corr[h];
+          const float wgt = sc[c][it] * cq[h];
+          const float sv = (float)dot * wgt;
+          if (ok) bm[h] = fmaxf(bm[h], sv);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float m = bm[h];
+        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+        m = fmaxf(m, dpp_f<kDppMirror>(m));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        bm[h] = m;
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (jl < nblk_split) sm.blk[jl][h] = bm[h];
+          else sm.xblk[jl - nblk_split][h] = bm[h];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // select: split-local Top-δ ([TS] Methodology 2, "Mechanism" and
 // "Pseudo-Max Approximation"; sink and local blocks always kept)
@@ -288,7 +397,7 @@ struct AttendState {
   float l;   // this lane's share of the normaliser
 };
 
-template <int D, int G, bool DENSE>
+template <int D, int G, bool DENSE, bool THUMB>
 __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
                                               int L, int lane, int w, AttendState<D>& st) {
   constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
@@ -339,14 +448,34 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     const uint16_t* kb = p.k + r0 * D;   // token t of this block is row t - t0
     const uint16_t* vb = p.v + r0 * D;
 
-    // ---- issue the block's loads: K into registers, V into registers ----
+    // ---- issue the block's loads: K (or its thumbnail + residual) and V ----
     u32x4_t kr[4][KS];
+    uint32_t kc[4][(D / 64) > 0 ? D / 64 : 1];   // thumbnail codes (16 per word)
+    u32x2_t kres[4][KS];                          // residual bytes, 8 per k-step
+    if constexpr (!THUMB) {
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const int t = min(t0 + 16 * T + h, tlast);
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)(t - t0) * D + g * (D / 4));
+      for (int T = 0; T < 4; ++T) {
+        const int t = min(t0 + 16 * T + h, tlast);
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)(t - t0) * D + g * (D / 4));
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kr[T][s] = src[s];
+        for (int s = 0; s < KS; ++s) kr[T][s] = src[s];
+      }
+    } else {
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const int t = min(t0 + 16 * T + h, tlast);
+        const uint8_t* cs = p.k2 + (r0 + (size_t)(t - t0)) * (D / 4) + g * (D / 16);
+        if constexpr (D == 128) {
+          const u32x2_t u = *reinterpret_cast<const u32x2_t*>(cs);
+          kc[T][0] = u.x;
+          kc[T][1] = u.y;
+        } else {
+          kc[T][0] = *reinterpret_cast<const uint32_t*>(cs);
+        }
+        const u32x2_t* rs = reinterpret_cast<const u32x2_t*>(p.kr + (r0 + (size_t)(t - t0)) * D + g * (D / 4));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kres[T][s] = rs[s];
+      }
     }
     u32x4_t vr[VL];
 #pragma unroll
@@ -359,12 +488,44 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
 
     // ---- QK on the matrix cores ----
     f32x4_t sacc[4];
+    if constexpr (!THUMB) {
 #pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      sacc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int T = 0; T < 4; ++T) {
+        sacc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[T][s]), qop[s], sacc[T], 0, 0, 0);
+        for (int s = 0; s < KS; ++s)
+          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[T][s]), qop[s], sacc[T], 0, 0, 0);
+      }
+    } else {
+      // q.K^ = t * (2 q.u - 3 sum q) + s8 * q.r8: u and r8 are small integers,
+      // exact in bf16, so both dot products run on the matrix cores exactly up
+      // to fp32 accumulation and K^ is never formed.
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t ar = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const uint32_t cbits = kc[T][s >> 1] >> (16 * (s & 1));
+          bf16x8_t a_u, a_r;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            a_u[e] = (__bf16)(float)((cbits >> (2 * e)) & 3u);
+            const uint32_t word = (e < 4) ? kres[T][s].x : kres[T][s].y;
+            a_r[e] = (__bf16)(float)(int8_t)(word >> (8 * (e & 3)));
+          }
+          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_u, qop[s], au, 0, 0, 0);
+          ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_r, qop[s], ar, 0, 0, 0);
+        }
+        const float qs = (h < G) ? sm.qsumf[h] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = min(t0 + 16 * T + 4 * g + r, tlast);
+          const float ts = p.k2scale[r0 + (t - t0)];
+          const float s8 = p.krscale[r0 + (t - t0)];
+          sacc[T][r] = ts * (2.f * au[r] - 3.f * qs) + s8 * ar[r];
+        }
+      }
     }
 
     // ---- V tile to LDS (this wave's region) ----
@@ -458,7 +619,7 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, flo
   else static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(v);
 }
 
-template <int D, int G, bool DENSE>
+template <int D, int G, bool DENSE, bool THUMB>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodeParams p) {
   __shared__ DecodeSmem<D, G> sm;
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
@@ -508,6 +669,14 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
       amax = fmaxf(amax, fabsf(x[r]));
     }
     amax = wave_max_f(amax);
+    if constexpr (THUMB) {
+      float fs = 0.f;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) fs += x[r];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) fs += __shfl_xor(fs, o);
+      if (lane == 0) sm.qsumf[h] = fs;
+    }
     int qsum = 0;
     if constexpr (!DENSE) {
       // amax < 2^-120 counts as a zero query: 127/amax would overflow to +inf
@@ -541,7 +710,8 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     // sink/local pseudo-max: the sink and local blocks outside this split are
     // listed in the prologue and scanned in the same pass as the split
     const int nx = p.pm_sink_local ? sm.nx : 0;
-    scan_blocks<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
+    if constexpr (THUMB) scan_blocks_thumb<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
+    else scan_blocks<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
     __syncthreads();
     if (p.pm_sink_local && tid < G) {
       float m = -INFINITY;
@@ -559,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 
   // ---- attend -------------------------------------------------------------
   AttendState<D> st;
-  attend_blocks<D, G, DENSE>(p, sm, b, j, j0, L, lane, w, st);
+  attend_blocks<D, G, DENSE, THUMB>(p, sm, b, j, j0, L, lane, w, st);
 
   // this wave's partial: normaliser of head h summed over its 4 lane groups
   float lw = st.l;
@@ -649,11 +819,11 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
   }
 }
 
-template <int D, int G, bool DENSE>
+template <int D, int G, bool DENSE, bool THUMB>
 hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) {
   if ((static_cast<int>(stage) & static_cast<int>(Stage::kPartials)) && p.n_splits > 0) {
     dim3 grid(p.n_splits, p.Hkv, p.B);
-    fused_decode_kernel<D, G, DENSE><<<grid, kThreads, 0, stream>>>(p);
+    fused_decode_kernel<D, G, DENSE, THUMB><<<grid, kThreads, 0, stream>>>(p);
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
     combine_kernel<D><<<dim3(p.Hq, p.B), 512, 0, stream>>>(p);
@@ -661,22 +831,30 @@ hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool THUMB>
 hipError_t launch_g(const DecodeParams& p, int G, Stage stage, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_fused<D, 1, DENSE>(p, stage, stream);
-    case 2: return launch_fused<D, 2, DENSE>(p, stage, stream);
-    case 4: return launch_fused<D, 4, DENSE>(p, stage, stream);
-    case 8: return launch_fused<D, 8, DENSE>(p, stage, stream);
+    case 1: return launch_fused<D, 1, DENSE, THUMB>(p, stage, stream);
+    case 2: return launch_fused<D, 2, DENSE, THUMB>(p, stage, stream);
+    case 4: return launch_fused<D, 4, DENSE, THUMB>(p, stage, stream);
+    case 8: return launch_fused<D, 8, DENSE, THUMB>(p, stage, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int D, bool THUMB>
+hipError_t launch_dt(const DecodeParams& p, int G, bool dense, Stage stage, hipStream_t stream) {
+  return dense ? launch_g<D, true, THUMB>(p, G, stage, stream) : launch_g<D, false, THUMB>(p, G, stage, stream);
+}
+
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream) {
-  if (D == 128) return dense ? launch_g<128, true>(p, G, stage, stream) : launch_g<128, false>(p, G, stage, stream);
-  if (D == 64) return dense ? launch_g<64, true>(p, G, stage, stream) : launch_g<64, false>(p, G, stage, stream);
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream,
+                         bool thumb) {
+  if (D == 128) return thumb ? launch_dt<128, true>(p, G, dense, stage, stream)
+                             : launch_dt<128, false>(p, G, dense, stage, stream);
+  if (D == 64) return thumb ? launch_dt<64, true>(p, G, dense, stage, stream)
+                            : launch_dt<64, false>(p, G, dense, stage, stream);
   return hipErrorInvalidValue;
 }
 

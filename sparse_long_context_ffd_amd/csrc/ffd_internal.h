@@ -18,6 +18,10 @@ struct DecodeParams {
   const uint16_t* v;       // bf16 [B, Hkv, cap, D]
   const uint8_t* kq;       // u8   [B, Hkv, cap, D/2]
   const float* kscale;     // f32  [B, Hkv, cap]
+  const uint8_t* k2;       // thumbnail storage: 2-bit codes u8 [B, Hkv, cap, D/4]
+  const float* k2scale;    //   f32 [B, Hkv, cap]  (t)
+  const int8_t* kr;        //   int8 residual [B, Hkv, cap, D]
+  const float* krscale;    //   f32 [B, Hkv, cap]  (s8)
   const int32_t* seq_lens; // [B]
   const int32_t* block_table;  // [B, table_stride] page of each block, or null (contiguous cache)
   int table_stride, num_pages; // paged cache: K/V [num_pages, Hkv, 64, D], kq/kscale alike
@@ -51,9 +55,15 @@ hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, con
                               const int32_t* pos_end, const int32_t* block_table, int table_stride, int num_pages,
                               int B, int Hkv, int cap, int D, int max_span, hipStream_t stream);
 
+hipError_t launch_quantize_thumb(const uint16_t* k, uint8_t* k2, float* k2scale, int8_t* kr, float* krscale,
+                                 const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int cap, int D,
+                                 int max_span, hipStream_t stream);
+
 enum class Stage { kPartials = 1, kCombine = 2, kBoth = 3 };
 
-// Returns hipErrorInvalidValue for an unsupported (D, G) pair.
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream);
+// Returns hipErrorInvalidValue for an unsupported (D, G) pair. thumb: K comes
+// from the thumbnail + residual storage instead of bf16 K and the int4 sketch.
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream,
+                         bool thumb = false);
 
 }  // namespace ffd

@@ -33,8 +33,8 @@ FFD_OUT_F32 = 1
 PSEUDO_MAX = {"split": 0, "sink_local": 1}
 
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_quantize_kv_paged",
-                    "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged", "ffd_decode_partials",
-                    "ffd_combine")
+                    "ffd_quantize_kv_thumb", "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged",
+                    "ffd_decode_thumb", "ffd_decode_partials", "ffd_combine")
 
 
 class FFDError(RuntimeError):
@@ -85,6 +85,14 @@ def lib() -> ctypes.CDLL:
                                    _i, ctypes.c_float, _i, _i, _i, _i,        # block_size delta sink local pm split
                                    ctypes.c_float, _vp, _i, _vp, _vp,         # sm_scale out out_dtype lse mask
                                    _vp, ctypes.c_size_t, _vp]                 # workspace bytes stream
+    L.ffd_quantize_kv_thumb.restype = _i
+    L.ffd_quantize_kv_thumb.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    L.ffd_decode_thumb.restype = _i
+    L.ffd_decode_thumb.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,          # q k2 k2s kr krs v seq_lens
+                                   _i, _i, _i, _i, _i, _i,                     # max_seq_len B Hq Hkv d cap
+                                   _i, ctypes.c_float, _i, _i, _i, _i,         # block_size delta sink local pm split
+                                   ctypes.c_float, _vp, _i, _vp, _vp,          # sm_scale out out_dtype lse mask
+                                   _vp, ctypes.c_size_t, _vp]                  # workspace bytes stream
     L.ffd_combine.restype = _i
     L.ffd_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _i, _vp, _vp]
     _lib = L
@@ -270,6 +278,63 @@ def ffd_decode_paged(q, k_pages, v_pages, kq_pages, kscale_pages, block_table, s
                                   Hkv, d, int(block_size), float(delta), int(sink), int(local), _pm(pseudo_max),
                                   int(split_blocks), float(sm_scale), _ptr(out), odt, _ptr(lse), _ptr(kept_mask),
                                   _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def ffd_quantize_kv_thumb(k, k2, k2scale, kr, krscale, pos_begin, pos_end, max_span: int, stream=None) -> None:
+    """Thumbnail + residual storage of bf16 K rows ``[pos_begin[b], pos_end[b])`` (in place)."""
+    _need(k, "k", torch.bfloat16, 4)
+    B, Hkv, cap, d = k.shape
+    _need(k2, "k2", torch.uint8, 4)
+    _need(k2scale, "k2scale", torch.float32, 3)
+    _need(kr, "kr", torch.int8, 4)
+    _need(krscale, "krscale", torch.float32, 3)
+    if (tuple(k2.shape) != (B, Hkv, cap, d // 4) or tuple(kr.shape) != (B, Hkv, cap, d)
+            or tuple(k2scale.shape) != (B, Hkv, cap) or tuple(krscale.shape) != (B, Hkv, cap)):
+        raise ValueError("thumbnail/residual shapes do not match k")
+    _check(lib().ffd_quantize_kv_thumb(_ptr(k), _ptr(k2), _ptr(k2scale), _ptr(kr), _ptr(krscale), _ptr(pos_begin),
+                                       _ptr(pos_end), B, Hkv, cap, d, int(max_span), _stream(stream)))
+
+
+def ffd_decode_thumb(q, k2, k2scale, kr, krscale, v, seq_lens, *, max_seq_len: int, block_size: int, delta: float,
+                     sink: int, local: int, split_blocks: int, sm_scale: float, out: torch.Tensor,
+                     lse: torch.Tensor, kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
+                     pseudo_max: str = "split", stream=None) -> None:
+    """One decode step over the thumbnail + residual key storage."""
+    _need(q, "q", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 4)
+    B, Hq, d = q.shape
+    _, Hkv, cap, _ = v.shape
+    _need(k2, "k2", torch.uint8, 4)
+    _need(k2scale, "k2scale", torch.float32, 3)
+    _need(kr, "kr", torch.int8, 4)
+    _need(krscale, "krscale", torch.float32, 3)
+    if (tuple(k2.shape) != (B, Hkv, cap, d // 4) or tuple(kr.shape) != (B, Hkv, cap, d)
+            or tuple(v.shape) != (B, Hkv, cap, d)):
+        raise ValueError("thumbnail/residual/v shapes do not match q")
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if kept_mask is not None:
+        _need(kept_mask, "kept_mask", torch.uint8, 3)
+        if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
+            raise ValueError("kept_mask shape")
+    odt = _check_outputs(out, lse, B, Hq, d)
+    _check(lib().ffd_decode_thumb(_ptr(q), _ptr(k2), _ptr(k2scale), _ptr(kr), _ptr(krscale), _ptr(v), _ptr(seq_lens),
+                                  int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta), int(sink),
+                                  int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out), odt,
+                                  _ptr(lse), _ptr(kept_mask), _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def quantize_kv_thumb(k: torch.Tensor, seq_lens: torch.Tensor, stream=None):
+    """Allocate and build the thumbnail + residual storage of ``k`` for tokens ``[0, seq_lens[b])``."""
+    B, Hkv, cap, d = k.shape
+    dev = k.device
+    k2 = torch.zeros((B, Hkv, cap, d // 4), dtype=torch.uint8, device=dev)
+    k2s = torch.zeros((B, Hkv, cap), dtype=torch.float32, device=dev)
+    kr = torch.zeros((B, Hkv, cap, d), dtype=torch.int8, device=dev)
+    krs = torch.zeros((B, Hkv, cap), dtype=torch.float32, device=dev)
+    begin = torch.zeros(B, dtype=torch.int32, device=dev)
+    ffd_quantize_kv_thumb(k, k2, k2s, kr, krs, begin, seq_lens.to(device=dev, dtype=torch.int32).contiguous(), cap,
+                          stream)
+    return k2, k2s, kr, krs
 
 
 # ---------------------------------------------------------------------------
