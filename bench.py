@@ -56,13 +56,21 @@ def host_cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def algorithmic_bytes(mask, seq_lens, Hkv: int, G: int, d: int, bs: int, dense: bool):
-    """Bytes the method must move for one step, from the kept-block mask."""
+def algorithmic_bytes(mask, seq_lens, Hkv: int, G: int, d: int, bs: int, dense: bool, storage: str = "int4"):
+    """Bytes the method must move for one step, from the kept-block mask.
+
+    int4: 68 B scan (d/2 codes + fp32 scale) per valid token, 4d B (bf16 K and V)
+    per valid token of a kept block. thumb: 36 B scan (d/4 codes + scale) per
+    valid token, d + 4 + 2d B (int8 residual + scale + bf16 V) per kept token."""
     import numpy as np
 
     B = mask.shape[0]
-    scan_tok = d // 2 + 4
-    kv_tok = 2 * d * 2
+    if storage == "thumb":
+        scan_tok = d // 4 + 4
+        kv_tok = d + 4 + 2 * d
+    else:
+        scan_tok = d // 2 + 4
+        kv_tok = 2 * d * 2
     scan = 0
     kv = 0
     kept_union = 0
@@ -99,7 +107,8 @@ def load_traffic(workload: str, delta: float, launches_bytes: float):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: str = "split"):
+def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: str = "split",
+                 storage: str = "int4"):
     """The oracle, as it stands, on a bounded sample of the same step: whole
     (sequence, kv head) groups in order, until ~budget_s of work is done."""
     import numpy as np
@@ -118,7 +127,7 @@ def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: st
                 O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
                          block_size=w.block_size, delta=delta, sink=w.sink, local=w.local,
                          split_blocks=w.split_blocks, sm_scale=np.float32(sm_scale), heads=heads,
-                         pseudo_max=pseudo_max)
+                         pseudo_max=pseudo_max, storage=storage)
                 t_total += time.perf_counter() - t0
                 done_heads += heads
                 if t_total >= budget_s:
@@ -135,6 +144,8 @@ def main() -> int:
     ap.add_argument("--delta", type=float, default=None, help="default: the workload's first delta")
     ap.add_argument("--pseudo-max", default="split", choices=["split", "sink_local"],
                     help="split-local max (default) or the sink/local estimate")
+    ap.add_argument("--storage", default="int4", choices=["int4", "thumb"],
+                    help="int4 sketch + bf16 K (default) or 2-bit thumbnails + int8 residuals")
     ap.add_argument("--paged", action="store_true",
                     help="keep the cache in a shuffled page pool and call ffd_decode_paged's kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -201,6 +212,14 @@ def main() -> int:
     torch.cuda.synchronize()
     quant_build_us = qb0.elapsed_time(qb1) * 1e3
 
+    if args.storage == "thumb":
+        if args.paged:
+            print("bench.py: --paged is only implemented for the int4 storage", file=sys.stderr)
+            return 2
+        k2, k2s, kr, krs = ffd.quantize_kv_thumb(k, seq)
+        del kq, ks
+        torch.cuda.synchronize()
+
     out = torch.empty((B, w.Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, w.Hq), dtype=torch.float32, device=dev)
     nb_max = -(-msl // w.block_size)
@@ -235,6 +254,14 @@ def main() -> int:
     def step(dl, ev=None):
         if ev is not None:
             ev[0].record()
+        if args.storage == "thumb":
+            ffd.ffd_decode_thumb(q, k2, k2s, kr, krs, v, seq, delta=dl, sink=w.sink, local=w.local,
+                                 sm_scale=sm_scale, out=out, lse=lse, kept_mask=mask, workspace=ws,
+                                 pseudo_max=args.pseudo_max, **kw)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
         if args.paged:
             # the two launches of ffd_decode_paged, with an event between them
             ffd.ffd_decode_paged(q, kp, vp, None if math.isinf(dl) else kqp, None if math.isinf(dl) else ksp,
@@ -270,7 +297,7 @@ def main() -> int:
     wall, fused_us, comb_us = timed(delta, args.steps, args.warmup)
     step_us_wall = wall / args.steps * 1e6
     m = mask.cpu().numpy()
-    scan_b, kv_b, union_keep = algorithmic_bytes(m, inp["seq_lens"], Hkv, G, d, w.block_size, dense)
+    scan_b, kv_b, union_keep = algorithmic_bytes(m, inp["seq_lens"], Hkv, G, d, w.block_size, dense, args.storage)
     alg_bytes = scan_b + kv_b
     head_keep = float(m[:, :, :].sum() / max(1, sum(-(-int(L) // w.block_size) for L in inp["seq_lens"]) * w.Hq))
     fused_avg = float(fused_us.mean())
@@ -297,11 +324,14 @@ def main() -> int:
             "delta": None if dense else delta, "sink_blocks": w.sink, "local_blocks": w.local,
             "split_blocks": w.split_blocks, "pseudo_max": args.pseudo_max, "out_dtype": "f32",
             "kv_layout": "paged (64-token pages, shuffled)" if args.paged else "contiguous",
+            "key_storage": ("2-bit thumbnail + int8 residual (K^ refinement)" if args.storage == "thumb"
+                            else "int4 sketch + bf16 K"),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": ("fused_decode_kernel + combine_kernel (ffd_decode_paged)" if args.paged else
-                       "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)"),
+                       "fused_decode_kernel<thumb> + combine_kernel (ffd_decode_thumb)" if args.storage == "thumb"
+                       else "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -327,7 +357,7 @@ def main() -> int:
     if not args.no_dense and not dense:
         wall_d, fused_d, _ = timed(math.inf, max(10, args.steps // 5), 3)
         md = mask.cpu().numpy()
-        _, kv_d, _ = algorithmic_bytes(md, inp["seq_lens"], Hkv, G, d, w.block_size, True)
+        _, kv_d, _ = algorithmic_bytes(md, inp["seq_lens"], Hkv, G, d, w.block_size, True, args.storage)
         rec["dense_delta_inf"] = {
             "us_per_step": round(wall_d / max(10, args.steps // 5) * 1e6, 2),
             "fused_median_us": round(float(np.median(fused_d)), 2),
@@ -336,7 +366,7 @@ def main() -> int:
         }
 
     if not args.no_cpu_baseline:
-        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget, args.pseudo_max)
+        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget, args.pseudo_max, args.storage)
         smask = np.zeros_like(m)
         for b, h in heads:
             smask[b, h] = m[b, h]
@@ -346,7 +376,8 @@ def main() -> int:
         for b, j in groups:
             sub = np.zeros((1, G, m.shape[2]), dtype=m.dtype)
             sub[0] = m[b, j * G:(j + 1) * G]
-            s_scan, s_kv, _ = algorithmic_bytes(sub, inp["seq_lens"][b:b + 1], 1, G, d, w.block_size, dense)
+            s_scan, s_kv, _ = algorithmic_bytes(sub, inp["seq_lens"][b:b + 1], 1, G, d, w.block_size, dense,
+                                                args.storage)
             sample_b += s_scan + s_kv
         rec["cpu_baseline"] = {
             "value": round(sample_b / t_cpu / 1e9, 4),

@@ -241,10 +241,12 @@ __device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeS
     corr[h] = 3 * sm.sumq[h];
     cq[h] = sm.cq[h];
   }
-  constexpr int kChunk = 4;
+  // Codes are half the bytes of the int4 sketch, so twice as many blocks are
+  // kept in flight per wave to keep the same bytes outstanding.
+  constexpr int kChunk = 8;
   for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
     uint32_t cw[kChunk][4][NW];
-    float sc[kChunk][4];
+    float sc[kChunk];   // scale of token 16*ql + quad of each block
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
@@ -265,8 +267,9 @@ __device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeS
           } else {
             cw[c][it][0] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src)) : 0u;
           }
-          sc[c][it] = ok ? __builtin_nontemporal_load(p.k2scale + r0 + (t - t0)) : 0.f;
         }
+        const int ts = 16 * ql + quad;
+        sc[c] = (t0 + ts < L) ? __builtin_nontemporal_load(p.k2scale + r0 + ts) : 0.f;
       }
     }
 #pragma unroll
@@ -290,11 +293,13 @@ __device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeS
 #pragma unroll
             for (int h = 0; h < G; ++h) acc[h] = __builtin_amdgcn_sdot4(bytes, qp[h][i][k], acc[h], false);
           }
-        const bool ok = t0 + it * 16 + quad < L;
+        // every lane of the quad holds token it*16 + quad's dot; the lane with
+        // ql == it also holds its scale
+        const bool ok = (ql == it) && (t0 + it * 16 + quad < L);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const int dot = 2 * quad_sum_i(acc[h]) - corr[h];
-          const float wgt = sc[c][it] * cq[h];
+          const float wgt = sc[c] * cq[h];
           const float sv = (float)dot * wgt;
           if (ok) bm[h] = fmaxf(bm[h], sv);
         }
@@ -302,6 +307,8 @@ __device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeS
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float m = bm[h];
+        m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+        m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
         m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
         m = fmaxf(m, dpp_f<kDppMirror>(m));
         m = fmaxf(m, __shfl_xor(m, 16));
@@ -452,6 +459,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     u32x4_t kr[4][KS];
     uint32_t kc[4][(D / 64) > 0 ? D / 64 : 1];   // thumbnail codes (16 per word)
     u32x2_t kres[4][KS];                          // residual bytes, 8 per k-step
+    float tsl = 0.f, s8l = 0.f;                   // thumbnail and residual scales
     if constexpr (!THUMB) {
 #pragma unroll
       for (int T = 0; T < 4; ++T) {
@@ -476,10 +484,18 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
 #pragma unroll
         for (int s = 0; s < KS; ++s) kres[T][s] = rs[s];
       }
+      // per-token scales: lane l holds those of row l of the block
+      const int tl = min(t0 + lane, tlast) - t0;
+      tsl = p.k2scale[r0 + tl];
+      s8l = p.krscale[r0 + tl];
     }
+    // The thumbnail QK holds more registers (two accumulators, operand
+    // conversion), so only a quarter of V is in flight across it: the whole
+    // tile would cost the second wave per SIMD.
+    constexpr int VH = THUMB ? VL / 4 : VL;
     u32x4_t vr[VL];
 #pragma unroll
-    for (int n = 0; n < VL; ++n) {
+    for (int n = 0; n < VH; ++n) {
       const int f = n * kWave + lane;        // chunk id within the tile
       const int r = f / VC, q = f % VC;
       const int t = min(t0 + r, tlast);
@@ -520,12 +536,21 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
         const float qs = (h < G) ? sm.qsumf[h] : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = min(t0 + 16 * T + 4 * g + r, tlast);
-          const float ts = p.k2scale[r0 + (t - t0)];
-          const float s8 = p.krscale[r0 + (t - t0)];
+          const int src = 16 * T + 4 * g + r;   // the lane holding this row's scales
+          const float ts = __shfl(tsl, src);
+          const float s8 = __shfl(s8l, src);
           sacc[T][r] = ts * (2.f * au[r] - 3.f * qs) + s8 * ar[r];
         }
+        __builtin_amdgcn_sched_barrier(0);   // convert tile by tile: bounds live registers
       }
+    }
+
+#pragma unroll
+    for (int n = VH; n < VL; ++n) {
+      const int f = n * kWave + lane;        // chunk id within the tile
+      const int r = f / VC, q = f % VC;
+      const int t = min(t0 + r, tlast);
+      vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)(t - t0) * D + q * 8));
     }
 
     // ---- V tile to LDS (this wave's region) ----
