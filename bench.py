@@ -92,10 +92,15 @@ def algorithmic_bytes(mask, seq_lens, Hkv: int, G: int, d: int, bs: int, dense: 
     return scan, kv, (kept_union / blocks if blocks else 0.0)
 
 
-def load_traffic(workload: str, delta: float, launches_bytes: float):
+def profile_stem(workload: str, storage: str) -> str:
+    """File stem of the committed rocprofv3 summaries for one workload and key storage."""
+    return f"fused_decode_{'thumb_' if storage == 'thumb' else ''}{workload}"
+
+
+def load_traffic(workload: str, delta: float, mode: dict):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"fused_decode_{workload}_pmc.json")
+    was taken on the current kernel source in the same mode; else None."""
+    path = os.path.join(PROFILE_DIR, profile_stem(workload, mode["storage"]) + "_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -103,6 +108,8 @@ def load_traffic(workload: str, delta: float, launches_bytes: float):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     if rec.get("delta") != (None if math.isinf(delta) else delta):
+        return None
+    if rec.get("mode", {"storage": "int4", "pseudo_max": "split", "paged": False}) != mode:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -336,7 +343,8 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(w.name, delta, alg_bytes),
+            "traffic": load_traffic(w.name, delta, {"storage": args.storage, "pseudo_max": args.pseudo_max,
+                                                      "paged": bool(args.paged)}),
             "algorithmic_bytes_per_launch": int(alg_bytes),
             "avg_launch_us": round(fused_avg, 2),
         },
