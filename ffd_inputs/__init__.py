@@ -13,4 +13,5 @@ from .gen import (  # noqa: F401
     f32_from_bf16_bits,
     make_inputs,
     make_random_inputs,
+    multi_query,
 )

@@ -194,3 +194,25 @@ def make_random_inputs(B: int, Hq: int, Hkv: int, d: int, lens, seed: int, block
                  bias="hot" if hot_frac > 0 else "none", hot_frac=hot_frac, alpha=tuple(alpha),
                  cap=cap)
     return make_inputs(w, poison_tail=poison_tail)
+
+
+def multi_query(inp: dict, Q: int, seed: int, rho: float = 0.8) -> np.ndarray:
+    """Q query tokens per sequence for a multi-query step over ``inp``'s cache.
+
+    Token Q-1 (the newest) is ``inp["q"]`` itself, so the workload's hot
+    blocks stay aligned with it; the earlier tokens are correlated with it like
+    consecutive decode positions: ``rho * q + sqrt(1 - rho^2) * z`` with
+    ``z ~ N(0, 1)`` from ``SeedSequence(seed)``, rounded to bf16. Returns bf16
+    bits ``[B, Q, Hq, d]``."""
+    q = f32_from_bf16_bits(inp["q"])
+    B, Hq, d = q.shape
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    out = np.empty((B, Q, Hq, d), dtype=np.uint16)
+    for i in range(Q):
+        if i == Q - 1:
+            out[:, i] = inp["q"]
+        else:
+            z = rng.standard_normal((B, Hq, d), dtype=np.float32)
+            out[:, i] = bf16_bits_from_f32((np.float32(rho) * q + np.float32(math.sqrt(1 - rho * rho)) * z)
+                                           .astype(np.float32))
+    return out

@@ -10,6 +10,7 @@ from .ffd_oracle import (  # noqa: F401
     bf16_bits_to_f32,
     block_scores,
     decode,
+    decode_multi,
     pack_int4,
     quantize_cache,
     quantize_keys,

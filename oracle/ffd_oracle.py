@@ -56,6 +56,15 @@ for refinement). The formats are not given there; this library fixes them:
 * the scan uses the thumbnail: dot = sum qc * (2u - 3) (exact integer),
   s^ = fl32(float(dot) * fl32(t * cq)).
 
+Several query tokens per step (multi-query decode, :func:`decode_multi`): the
+pages describe one query token per decode step. This library's reading for Q
+tokens (a speculative-decoding verify step, or a chunk of new tokens): their
+keys and values are already in the cache, token i of a sequence of length L
+sits at position L - Q + i and sees rows 0 .. L - Q + i, so it is one decode
+step of length L - Q + 1 + i with its own selection. A GPU kernel may share
+the scan and the kept blocks between the Q tokens; the result is defined per
+token.
+
 Floating point: every selection step is done in explicit np.float32 scalars
 and arrays (no Python floats, which would promote to fp64), so the kept-block
 mask is reproducible bit for bit. Attention is done in fp64.
@@ -401,6 +410,45 @@ def decode(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink:
                 o, s = attend(q32.astype(np.float64), k64[tok_keep], v64[tok_keep], sm_scale)
                 out[b, h] = o
                 lse[b, h] = s
+    return out, lse, mask
+
+
+def decode_multi(q, k, v, seq_lens, *, max_seq_len: int, block_size: int, delta, sink: int, local: int,
+                 split_blocks: int, sm_scale=None, quantize: bool = True, heads=None, mask_only: bool = False,
+                 pseudo_max: str = "split"):
+    """Several query tokens per sequence in one step (multi-query decode).
+
+    The pages describe one query token per step. This library's reading for Q
+    query tokens: the cache already holds the keys and values of all Q new
+    tokens, query token i of sequence b sits at position ``seq_lens[b] - Q + i``
+    and sees the rows up to and including its own position. Each query token
+    is therefore exactly one decode step of :func:`decode` with sequence length
+    ``seq_lens[b] - Q + 1 + i`` (then capped by ``max_seq_len``; a length <= 0
+    is an empty step): its own scores, pseudo-max, Top-δ set and attention.
+
+    ``q`` bf16 bits ``[B, Q, Hq, d]``. Returns ``(out [B,Q,Hq,d], lse [B,Q,Hq],
+    mask uint8 [B,Q,Hq,NB_max])``. ``heads`` restricts the work to ``(b, i, h)``
+    triples.
+    """
+    q = np.asarray(q)
+    B, Q, Hq, d = q.shape
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    nb_max = -(-max_seq_len // block_size)
+    out = np.full((B, Q, Hq, d), np.nan)
+    lse = np.full((B, Q, Hq), np.nan)
+    mask = np.zeros((B, Q, Hq, nb_max), dtype=np.uint8)
+    for i in range(Q):
+        hs = None
+        if heads is not None:
+            hs = [(b, h) for (b, qi, h) in heads if qi == i]
+            if not hs:
+                continue
+        o, s, m = decode(q[:, i], k, v, lens - Q + 1 + i, max_seq_len=max_seq_len, block_size=block_size,
+                         delta=delta, sink=sink, local=local, split_blocks=split_blocks, sm_scale=sm_scale,
+                         quantize=quantize, heads=hs, mask_only=mask_only, pseudo_max=pseudo_max)
+        out[:, i] = o
+        lse[:, i] = s
+        mask[:, i] = m
     return out, lse, mask
 
 

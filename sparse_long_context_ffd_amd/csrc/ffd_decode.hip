@@ -11,8 +11,8 @@
 // one (sequence b, kv head j) and serves all G = Hq/Hkv query heads of the
 // group, so every K/V byte it reads is shared by the G heads.
 //
-//  prologue  q[b, jG..jG+G) -> LDS: fp32 copy (pre-scaled by sm_scale*log2 e)
-//            and int8 copy + per-head scale (the scan query).
+//  prologue  q[b, jG..jG+G) -> LDS: fp32 copy and int8 copy + per-head scale
+//            (the scan query).
 //  scan      each wave takes whole blocks; a quad of lanes owns one token (each
 //            lane 16 B of int4 codes for D=128), 16 tokens per wave load =
 //            1 KiB contiguous. Nibbles are moved to offset binary (x ^ 8 =
@@ -54,9 +54,15 @@ constexpr int kWaves = kThreads / kWave;
 
 template <int D, int G>
 struct DecodeSmem {
-  uint16_t vt[kWaves][kBlockSize * D];  // per-wave V tile (bf16, swizzled rows)
-  float q[G][D];            // bf16 query widened to fp32 (prologue only)
+  // The V tiles are live only during attend: the prologue's fp32 query and
+  // the epilogue's per-wave partial outputs reuse their space.
+  union {
+    uint16_t vt[kWaves][kBlockSize * D];  // per-wave V tile (bf16, swizzled rows)
+    float q[G][D];                        // bf16 query widened to fp32 (prologue)
+    float wo[kWaves][G][D];               // per-wave partial outputs (epilogue)
+  };
   int8_t qc[G][D];          // int8 scan query
+  static_assert(sizeof(float) * G <= sizeof(uint16_t) * kBlockSize, "wave partials must fit the V tiles");
   float cq[G];              // fl32(sq * sm_scale)
   int sumq[G];              // sum of qc (offset-binary correction)
   float qsumf[G];           // sum of the bf16 query (thumbnail refinement correction)
@@ -72,7 +78,6 @@ struct DecodeSmem {
   int nkept;
   float wm[kWaves][G];
   float wl[kWaves][G];
-  float wo[kWaves][G][D];
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -683,7 +688,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     sm.nx = nx;
   }
   __syncthreads();
-  const float qscale = p.sm_scale * kLog2e;
   for (int h = w; h < G; h += kWaves) {
     constexpr int PER = D / kWave;
     float x[PER];
@@ -725,8 +729,6 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
         sm.cq[h] = nz ? (amax / 127.0f) * p.sm_scale : 0.f;
       }
     }
-#pragma unroll
-    for (int r = 0; r < PER; ++r) sm.q[h][lane + r * kWave] = x[r] * qscale;
   }
   __syncthreads();
 
@@ -756,7 +758,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   AttendState<D> st;
   attend_blocks<D, G, DENSE, THUMB>(p, sm, b, j, j0, L, lane, w, st);
 
-  // this wave's partial: normaliser of head h summed over its 4 lane groups
+  // this wave's partial: normaliser of head h summed over its 4 lane groups;
+  // the partial outputs overwrite the V tiles, so every wave must be done
+  __syncthreads();
   float lw = st.l;
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
