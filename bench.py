@@ -115,9 +115,11 @@ def load_traffic(workload: str, delta: float, mode: dict):
 
 
 def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: str = "split",
-                 storage: str = "int4"):
+                 storage: str = "int4", qm=None):
     """The oracle, as it stands, on a bounded sample of the same step: whole
-    (sequence, kv head) groups in order, until ~budget_s of work is done."""
+    (sequence, kv head) groups in order, until ~budget_s of work is done.
+    ``qm`` (bf16 bits [B, Q, Hq, d]): a multi-query step, every query token of
+    the group's heads."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -131,10 +133,17 @@ def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: st
             for j in range(w.Hkv):
                 heads = [(b, h) for h in range(j * G, (j + 1) * G)]
                 t0 = time.perf_counter()
-                O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
-                         block_size=w.block_size, delta=delta, sink=w.sink, local=w.local,
-                         split_blocks=w.split_blocks, sm_scale=np.float32(sm_scale), heads=heads,
-                         pseudo_max=pseudo_max, storage=storage)
+                if qm is None:
+                    O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
+                             block_size=w.block_size, delta=delta, sink=w.sink, local=w.local,
+                             split_blocks=w.split_blocks, sm_scale=np.float32(sm_scale), heads=heads,
+                             pseudo_max=pseudo_max, storage=storage)
+                else:
+                    O.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
+                                   block_size=w.block_size, delta=delta, sink=w.sink, local=w.local,
+                                   split_blocks=w.split_blocks, sm_scale=np.float32(sm_scale),
+                                   heads=[(bb, i, h) for bb, h in heads for i in range(qm.shape[1])],
+                                   pseudo_max=pseudo_max)
                 t_total += time.perf_counter() - t0
                 done_heads += heads
                 if t_total >= budget_s:
@@ -153,6 +162,8 @@ def main() -> int:
                     help="split-local max (default) or the sink/local estimate")
     ap.add_argument("--storage", default="int4", choices=["int4", "thumb"],
                     help="int4 sketch + bf16 K (default) or 2-bit thumbnails + int8 residuals")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="query tokens per sequence (ffd_decode_multi; token i sees the cache up to L - Q + i)")
     ap.add_argument("--paged", action="store_true",
                     help="keep the cache in a shuffled page pool and call ffd_decode_paged's kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -172,7 +183,7 @@ def main() -> int:
     import torch
 
     import sparse_long_context_ffd_amd as ffd
-    from ffd_inputs import WORKLOADS, make_inputs
+    from ffd_inputs import WORKLOADS, make_inputs, multi_query
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -227,11 +238,18 @@ def main() -> int:
         del kq, ks
         torch.cuda.synchronize()
 
-    out = torch.empty((B, w.Hq, d), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, w.Hq), dtype=torch.float32, device=dev)
+    Q = args.queries
+    if Q > 1 and (args.paged or args.storage == "thumb"):
+        print("bench.py: --queries is only implemented for the contiguous int4 storage", file=sys.stderr)
+        return 2
+    qm_bits = multi_query(inp, Q, seed=w.seed + 1000) if Q > 1 else None
+    qm = bf16(qm_bits) if Q > 1 else None
+    rows = (Q,) if Q > 1 else ()
+    out = torch.empty((B,) + rows + (w.Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B,) + rows + (w.Hq,), dtype=torch.float32, device=dev)
     nb_max = -(-msl // w.block_size)
-    mask = torch.empty((B, w.Hq, nb_max), dtype=torch.uint8, device=dev)
-    ws = ffd.alloc_workspace(B, w.Hq, d, msl, w.block_size, w.split_blocks, dev)
+    mask = torch.empty((B,) + rows + (w.Hq, nb_max), dtype=torch.uint8, device=dev)
+    ws = ffd.alloc_workspace(B, Q * w.Hq, d, msl, w.block_size, w.split_blocks, dev)
     kw = dict(max_seq_len=msl, block_size=w.block_size, split_blocks=w.split_blocks)
 
     if args.paged:
@@ -261,6 +279,14 @@ def main() -> int:
     def step(dl, ev=None):
         if ev is not None:
             ev[0].record()
+        if Q > 1:
+            ffd.ffd_decode_multi(qm, k, v, None if math.isinf(dl) else kq, None if math.isinf(dl) else ks, seq,
+                                 delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale, out=out, lse=lse,
+                                 kept_mask=mask, workspace=ws, pseudo_max=args.pseudo_max, **kw)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
         if args.storage == "thumb":
             ffd.ffd_decode_thumb(q, k2, k2s, kr, krs, v, seq, delta=dl, sink=w.sink, local=w.local,
                                  sm_scale=sm_scale, out=out, lse=lse, kept_mask=mask, workspace=ws,
@@ -304,9 +330,15 @@ def main() -> int:
     wall, fused_us, comb_us = timed(delta, args.steps, args.warmup)
     step_us_wall = wall / args.steps * 1e6
     m = mask.cpu().numpy()
+    if Q > 1:
+        m_rows = m
+        m = m.max(axis=1)   # a block is read once when any query token keeps it
     scan_b, kv_b, union_keep = algorithmic_bytes(m, inp["seq_lens"], Hkv, G, d, w.block_size, dense, args.storage)
     alg_bytes = scan_b + kv_b
     head_keep = float(m[:, :, :].sum() / max(1, sum(-(-int(L) // w.block_size) for L in inp["seq_lens"]) * w.Hq))
+    if Q > 1:
+        vis = sum(-(-max(0, int(L) - Q + 1 + i) // w.block_size) for L in inp["seq_lens"] for i in range(Q))
+        head_keep = float(m_rows.sum() / max(1, vis * w.Hq))
     fused_avg = float(fused_us.mean())
     achieved = alg_bytes / (fused_avg * 1e-6) / 1e9
     value = alg_bytes / (step_us_wall * 1e-6) / 1e9
@@ -331,20 +363,23 @@ def main() -> int:
             "delta": None if dense else delta, "sink_blocks": w.sink, "local_blocks": w.local,
             "split_blocks": w.split_blocks, "pseudo_max": args.pseudo_max, "out_dtype": "f32",
             "kv_layout": "paged (64-token pages, shuffled)" if args.paged else "contiguous",
+            "query_tokens": Q,
             "key_storage": ("2-bit thumbnail + int8 residual (K^ refinement)" if args.storage == "thumb"
                             else "int4 sketch + bf16 K"),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": ("fused_decode_kernel + combine_kernel (ffd_decode_paged)" if args.paged else
-                       "fused_decode_kernel<thumb> + combine_kernel (ffd_decode_thumb)" if args.storage == "thumb"
+                       f"fused_decode_kernel<{Q} query tokens> + combine_kernel (ffd_decode_multi)" if Q > 1
+                       else "fused_decode_kernel<thumb> + combine_kernel (ffd_decode_thumb)" if args.storage == "thumb"
                        else "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)"),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(w.name, delta, {"storage": args.storage, "pseudo_max": args.pseudo_max,
-                                                      "paged": bool(args.paged)}),
+            "traffic": None if Q > 1 else load_traffic(w.name, delta, {"storage": args.storage,
+                                                                         "pseudo_max": args.pseudo_max,
+                                                                         "paged": bool(args.paged)}),
             "algorithmic_bytes_per_launch": int(alg_bytes),
             "avg_launch_us": round(fused_avg, 2),
         },
@@ -365,6 +400,8 @@ def main() -> int:
     if not args.no_dense and not dense:
         wall_d, fused_d, _ = timed(math.inf, max(10, args.steps // 5), 3)
         md = mask.cpu().numpy()
+        if Q > 1:
+            md = md.max(axis=1)
         _, kv_d, _ = algorithmic_bytes(md, inp["seq_lens"], Hkv, G, d, w.block_size, True, args.storage)
         rec["dense_delta_inf"] = {
             "us_per_step": round(wall_d / max(10, args.steps // 5) * 1e6, 2),
@@ -374,7 +411,8 @@ def main() -> int:
         }
 
     if not args.no_cpu_baseline:
-        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget, args.pseudo_max, args.storage)
+        t_cpu, heads = cpu_baseline(inp, w, delta, sm_scale, args.cpu_budget, args.pseudo_max, args.storage,
+                                    qm_bits)
         smask = np.zeros_like(m)
         for b, h in heads:
             smask[b, h] = m[b, h]

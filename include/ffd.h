@@ -201,6 +201,41 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ffd_decode_multi -- Q query tokens per sequence in one call (a speculative
+ * verify step, or several new tokens at once). The pages describe one query
+ * token per decode step ([TS] Problem Statement; Methodology 3); this call
+ * applies the same step to each of Q tokens whose keys and values are already
+ * in the cache: token i of sequence b sits at position seq_lens[b] - Q + i and
+ * sees the rows before and at its own position, so its result is exactly that
+ * of ffd_decode with seq_lens[b] - Q + 1 + i in place of seq_lens[b] (own
+ * scores, pseudo-max, Top-δ set, sink/local range and attention; a length
+ * <= 0 gives out 0, lse -INFINITY and a zero mask row). The Q tokens share
+ * one pass over the int4 sketch (their scores are one small integer matrix
+ * product per tile, [TS] Significance: scanning is cheap compute) and one
+ * read of the blocks any of them keeps.
+ *   q          bf16 [B, Q, Hq, d]
+ *   out        [B, Q, Hq, d];  lse f32 [B, Q, Hq]
+ *   kept_mask  uint8 [B, Q, Hq, ceil(max_seq_len / block_size)] or NULL
+ *   workspace  >= ffd_decode_multi_workspace_bytes(B, Q, Hq, d, max_seq_len,
+ *              block_size, split_blocks) bytes, 256-byte aligned
+ * Everything else as ffd_decode. Supported: Q >= 1 with (Hq / Hkv) * Q <= 16;
+ * with FFD_PSEUDO_MAX_SINK_LOCAL, sink_blocks + local_blocks +
+ * ceil((Q - 1) / 64) <= 64. FFD_ERR_UNSUPPORTED otherwise. Q == 1 is ffd_decode.
+ */
+ffd_status ffd_decode_multi(const void* q, const void* k, const void* v,
+                            const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
+                            int max_seq_len, int B, int Q, int Hq, int Hkv, int d, int cap,
+                            int block_size, float delta, int sink_blocks, int local_blocks,
+                            int pseudo_max, int split_blocks, float sm_scale,
+                            void* out, int out_dtype, float* lse, uint8_t* kept_mask,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for ffd_decode_multi (the partials of Q * Hq query rows);
+ * 0 for unsupported sizes. */
+size_t ffd_decode_multi_workspace_bytes(int B, int Q, int Hq, int d, int max_seq_len,
+                                        int block_size, int split_blocks);
+
+/*
  * ffd_decode_paged -- ffd_decode on a paged KV cache (a block table instead of
  * one contiguous cache per sequence, as serving engines keep it). Pages are laid
  * out as for ffd_quantize_kv_paged (K and V pages bf16 [num_pages, Hkv, 64, d]);

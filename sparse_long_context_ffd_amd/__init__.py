@@ -17,9 +17,12 @@ from .ffd import (  # noqa: F401
     LIB_PATH,
     alloc_workspace,
     decode,
+    decode_multi,
     ffd_abi_version,
     ffd_combine,
     ffd_decode,
+    ffd_decode_multi,
+    ffd_decode_multi_workspace_bytes,
     ffd_decode_paged,
     ffd_decode_partials,
     ffd_decode_thumb,

@@ -113,6 +113,12 @@ ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* 
                          num_pages, B, Hkv, table_stride * ffd::kBlockSize, d, max_span, stream);
 }
 
+size_t ffd_decode_multi_workspace_bytes(int B, int Q, int Hq, int d, int max_seq_len, int block_size,
+                                        int split_blocks) {
+  if (Q <= 0 || Hq <= 0 || (long)Q * Hq > 65535) return 0;
+  return ffd_decode_workspace_bytes(B, Q * Hq, d, max_seq_len, block_size, split_blocks);
+}
+
 size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int block_size, int split_blocks) {
   if (B <= 0 || Hq <= 0 || d <= 0 || max_seq_len <= 0 || block_size != ffd::kBlockSize || split_blocks < 1) return 0;
   const int ns = n_splits_for(max_seq_len, split_blocks);
@@ -127,14 +133,14 @@ namespace {
 // and fills `p` (except the output fields). `need_bytes` gets the workspace
 // size the call requires.
 ffd_status prepare_decode(const char* fn, const void* q, const void* k, const void* v, const uint8_t* kq,
-                          const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv,
+                          const float* kscale, const int32_t* seq_lens, int max_seq_len, int B, int Q, int Hq, int Hkv,
                           int d, int cap, int block_size, float delta, int sink_blocks, int local_blocks,
                           int pseudo_max, int split_blocks, float sm_scale, uint8_t* kept_mask, void* workspace,
                           size_t workspace_bytes, const int32_t* block_table, int table_stride, int num_pages,
                           ffd::DecodeParams& p, int& G, bool& dense) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || cap < 0 || max_seq_len < 0)
-    return fail(FFD_ERR_INVALID_ARG, "%s: bad sizes (B=%d Hq=%d Hkv=%d cap=%d max_seq_len=%d)", fn, B, Hq, Hkv, cap,
-                max_seq_len);
+  if (B < 0 || Q < 1 || Hq <= 0 || Hkv <= 0 || cap < 0 || max_seq_len < 0)
+    return fail(FFD_ERR_INVALID_ARG, "%s: bad sizes (B=%d Q=%d Hq=%d Hkv=%d cap=%d max_seq_len=%d)", fn, B, Q, Hq, Hkv,
+                cap, max_seq_len);
   if (Hq % Hkv) return fail(FFD_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
   if (block_table == nullptr && cap < max_seq_len)
@@ -160,12 +166,19 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
   if (block_size != ffd::kBlockSize) return fail(FFD_ERR_UNSUPPORTED, "%s: block_size=%d not supported (64)", fn, block_size);
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(FFD_ERR_UNSUPPORTED, "%s: group size %d not supported (1, 2, 4, 8)", fn, G);
+  if ((long)G * Q > ffd::kMaxRows)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: %d query tokens x group size %d exceeds %d rows per workgroup", fn, Q, G,
+                ffd::kMaxRows);
   if (split_blocks > ffd::kMaxSplit)
     return fail(FFD_ERR_UNSUPPORTED, "%s: split_blocks=%d not supported (<= %d)", fn, split_blocks, ffd::kMaxSplit);
-  if (pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL && (long)sink_blocks + local_blocks > ffd::kMaxPseudoMax)
+  // the query tokens' local windows together span local + ceil((Q - 1) / 64) + 1 blocks at most
+  if (pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL &&
+      (long)sink_blocks + local_blocks + (Q > 1 ? (Q - 1 + ffd::kBlockSize - 1) / ffd::kBlockSize : 0) >
+          ffd::kMaxPseudoMax)
     return fail(FFD_ERR_UNSUPPORTED, "%s: sink_blocks + local_blocks = %ld exceeds %d with the sink/local pseudo-max",
                 fn, (long)sink_blocks + local_blocks, ffd::kMaxPseudoMax);
-  if (B > 65535 || Hkv > 65535 || Hq > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B, Hq, Hkv must be <= 65535", fn);
+  if (B > 65535 || Hkv > 65535 || (long)Q * Hq > 65535)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: B, Q * Hq, Hkv must be <= 65535", fn);
   dense = isinf(delta);
   if (B > 0) {
     if (!q || !seq_lens) return fail(FFD_ERR_INVALID_ARG, "%s: null q/seq_lens", fn);
@@ -177,7 +190,9 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   }
   const int nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
-  const size_t need = (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
+  const int rows = Q * Hq;   // query-head rows per sequence
+  const size_t need =
+      (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, rows, ns, d) + ffd::ws_lse_bytes(B, rows, ns) : 0;
   if (need > 0) {
     if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);
     if (workspace_bytes < need)
@@ -197,10 +212,11 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.num_pages = num_pages;
   char* ws = static_cast<char*>(workspace);
   p.o_part = need ? reinterpret_cast<float*>(ws) : nullptr;
-  p.lse_part = need ? reinterpret_cast<float*>(ws + ffd::ws_opart_bytes(B, Hq, ns, d)) : nullptr;
+  p.lse_part = need ? reinterpret_cast<float*>(ws + ffd::ws_opart_bytes(B, rows, ns, d)) : nullptr;
   p.mask = kept_mask;
   p.max_seq_len = max_seq_len;
   p.B = B;
+  p.Q = Q;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.cap = cap;
@@ -248,7 +264,7 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
   bool dense;
   ffd_status st = check_out_dtype("ffd_decode", out_dtype);
   if (st != FFD_OK) return st;
-  st = prepare_decode("ffd_decode", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d, cap, block_size,
+  st = prepare_decode("ffd_decode", q, k, v, kq, kscale, seq_lens, max_seq_len, B, 1, Hq, Hkv, d, cap, block_size,
                       delta, sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, workspace,
                       workspace_bytes, nullptr, 0, 0, p, G, dense);
   if (st != FFD_OK) return st;
@@ -258,6 +274,29 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v, const uint8_t
   p.lse = lse;
   p.out_f32 = out_dtype == FFD_OUT_F32;
   return launch("ffd_decode", p, d, G, dense, ffd::Stage::kBoth, stream);
+}
+
+ffd_status ffd_decode_multi(const void* q, const void* k, const void* v, const uint8_t* kq, const float* kscale,
+                            const int32_t* seq_lens, int max_seq_len, int B, int Q, int Hq, int Hkv, int d, int cap,
+                            int block_size, float delta, int sink_blocks, int local_blocks, int pseudo_max,
+                            int split_blocks, float sm_scale, void* out, int out_dtype, float* lse,
+                            uint8_t* kept_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "ffd_decode_multi";
+  ffd::DecodeParams p;
+  int G;
+  bool dense;
+  ffd_status st = check_out_dtype(fn, out_dtype);
+  if (st != FFD_OK) return st;
+  st = prepare_decode(fn, q, k, v, kq, kscale, seq_lens, max_seq_len, B, Q, Hq, Hkv, d, cap, block_size, delta,
+                      sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, workspace,
+                      workspace_bytes, nullptr, 0, 0, p, G, dense);
+  if (st != FFD_OK) return st;
+  st = check_out_ptrs(fn, B, out, lse);
+  if (st != FFD_OK) return st;
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = out_dtype == FFD_OUT_F32;
+  return launch(fn, p, d, G, dense, ffd::Stage::kBoth, stream);
 }
 
 ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pages, const uint8_t* kq_pages,
@@ -274,7 +313,7 @@ ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pa
   ffd_status st = check_out_dtype(fn, out_dtype);
   if (st != FFD_OK) return st;
   const int32_t* table = (max_seq_len > 0 && B > 0) ? block_table : nullptr;
-  st = prepare_decode(fn, q, k_pages, v_pages, kq_pages, kscale_pages, seq_lens, max_seq_len, B, Hq, Hkv, d,
+  st = prepare_decode(fn, q, k_pages, v_pages, kq_pages, kscale_pages, seq_lens, max_seq_len, B, 1, Hq, Hkv, d,
                       max_seq_len, block_size, delta, sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale,
                       kept_mask, workspace, workspace_bytes, table, table_stride, num_pages, p, G, dense);
   if (st != FFD_OK) return st;
@@ -302,7 +341,7 @@ ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2sca
     return fail(FFD_ERR_INVALID_ARG, "%s: null thumbnail/residual pointer", fn);
   if (!aligned16(k2) || !aligned16(kr)) return fail(FFD_ERR_INVALID_ARG, "%s: k2 and kr must be 16-byte aligned", fn);
   // the thumbnail codes stand in for the int4 sketch and K in the shared checks
-  st = prepare_decode(fn, q, v, v, k2, k2scale, seq_lens, max_seq_len, B, Hq, Hkv, d, cap, block_size, delta,
+  st = prepare_decode(fn, q, v, v, k2, k2scale, seq_lens, max_seq_len, B, 1, Hq, Hkv, d, cap, block_size, delta,
                       sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, workspace,
                       workspace_bytes, nullptr, 0, 0, p, G, dense);
   if (st != FFD_OK) return st;
@@ -332,7 +371,7 @@ ffd_status ffd_decode_partials(const void* q, const void* k, const void* v, cons
   ffd::DecodeParams p;
   int G;
   bool dense;
-  ffd_status st = prepare_decode("ffd_decode_partials", q, k, v, kq, kscale, seq_lens, max_seq_len, B, Hq, Hkv, d,
+  ffd_status st = prepare_decode("ffd_decode_partials", q, k, v, kq, kscale, seq_lens, max_seq_len, B, 1, Hq, Hkv, d,
                                  cap, block_size, delta, sink_blocks, local_blocks, pseudo_max, split_blocks,
                                  sm_scale, kept_mask, workspace, workspace_bytes, nullptr, 0, 0, p, G, dense);
   if (st != FFD_OK) return st;
@@ -377,6 +416,7 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   p.out_f32 = out_dtype == FFD_OUT_F32;
   p.max_seq_len = max_seq_len;
   p.B = B;
+  p.Q = 1;
   p.Hq = Hq;
   p.Hkv = 1;
   p.nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;

@@ -52,32 +52,35 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
-template <int D, int G>
+// R query rows per workgroup: R = G heads of the kv group for one query token,
+// or G x Q for Q query tokens (row r = token r / G, head r % G).
+template <int D, int R>
 struct DecodeSmem {
   // The V tiles are live only during attend: the prologue's fp32 query and
   // the epilogue's per-wave partial outputs reuse their space.
   union {
     uint16_t vt[kWaves][kBlockSize * D];  // per-wave V tile (bf16, swizzled rows)
-    float q[G][D];                        // bf16 query widened to fp32 (prologue)
-    float wo[kWaves][G][D];               // per-wave partial outputs (epilogue)
+    float q[R][D];                        // bf16 query widened to fp32 (prologue)
+    float wo[kWaves][R][D];               // per-wave partial outputs (epilogue)
   };
-  int8_t qc[G][D];          // int8 scan query
-  static_assert(sizeof(float) * G <= sizeof(uint16_t) * kBlockSize, "wave partials must fit the V tiles");
-  float cq[G];              // fl32(sq * sm_scale)
-  int sumq[G];              // sum of qc (offset-binary correction)
-  float qsumf[G];           // sum of the bf16 query (thumbnail refinement correction)
-  float blk[kMaxSplit][G];  // block scores of the split
+  int8_t qc[R][D];          // int8 scan query
+  static_assert(sizeof(float) * R <= sizeof(uint16_t) * kBlockSize, "wave partials must fit the V tiles");
+  static_assert(R <= kMaxRows, "at most 16 query rows per workgroup");
+  float cq[R];              // fl32(sq * sm_scale)
+  int sumq[R];              // sum of qc (offset-binary correction)
+  float qsumf[R];           // sum of the bf16 query (thumbnail refinement correction)
+  float blk[kMaxSplit][R];  // block scores of the split
   int xidx[kMaxPseudoMax];  // sink/local blocks outside the split (sink/local pseudo-max)
   int nx;
-  float xblk[kMaxPseudoMax][G];
-  float pm[G];              // sink/local pseudo-max per head
-  float seed[G];            // split max of the block scores (natural-log units)
+  float xblk[kMaxPseudoMax][R];
+  float pm[R];              // sink/local pseudo-max per row
+  float seed[R];            // split max of the block scores (natural-log units)
   int rowp[kMaxSplit];      // paged cache: first cache row of each block of the split
   uint8_t kidx[kMaxSplit];  // kept blocks (split-local index)
-  uint8_t khm[kMaxSplit];   // per-head keep bits of each kept block
+  uint16_t khm[kMaxSplit];  // per-row keep bits of each kept block
   int nkept;
-  float wm[kWaves][G];
-  float wl[kWaves][G];
+  float wm[kWaves][R];
+  float wl[kWaves][R];
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -85,6 +88,25 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// Query-head row of row r of the workgroup of (sequence b, kv head j): query
+// token r / G, head j * G + r % G. Rows index q, out, lse, mask and partials.
+template <int G>
+__device__ __forceinline__ size_t row_index(const DecodeParams& p, int b, int j, int r) {
+  return ((size_t)b * p.Q + r / G) * p.Hq + (size_t)j * G + r % G;
+}
+
+// Tokens row r may see: its query token i = r / G sits at position sl - Q + i
+// of a sequence of length sl, so it sees sl - Q + 1 + i tokens (capped by
+// max_seq_len). Rows past the Q tokens (padding) see none.
+template <int G>
+__device__ __forceinline__ int row_len(const DecodeParams& p, int sl, int r) {
+  const int i = r / G;
+  if (i >= p.Q) return 0;
+  const int L = sl - p.Q + 1 + i;
+  return L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+}
 
 // First cache row of block jb of (sequence b, kv head j). For a paged cache
 // the split's rows were looked up once into LDS (rowp); blocks outside the
@@ -331,43 +353,158 @@ __device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeS
   }
 }
 
+// Multi-query scan (Q > 1 query tokens, int4 sketch): the R = G x Q rows'
+// scores are one small integer matrix product per 16-token tile, done on the
+// matrix cores (v_mfma_i32_16x16x64_i8; exact int32): A = the int8 queries
+// (row n = lane % 16), B = the tile's codes moved to offset binary (code + 8,
+// token column n = lane % 16); lane group g = lane / 16 holds dims
+// g*D/4 .. +D/4 of both, in the order the nibbles are unpacked. Output lane
+// (g, n) holds rows 4g..4g+3 of token n; the 8*sum(q) excess is subtracted and
+// s^ = fl32(float(dot) * fl32(scale * cq)) as in the single-query scan. Each
+// row only counts the tokens its query token sees.
+template <int D, int G, int QT>
+__device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
+                                               int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
+  constexpr int R = G * QT;
+  constexpr int NM = D / 64;   // MFMAs per tile (k = 64 each)
+  const int nblk = nblk_split + nx;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  // A operand: word e of MFMA s holds dims g*D/4 + 8*(2s + e/2) + 2*i + (e & 1), i = 0..3
+  i32x4_t qa[NM];
+#pragma unroll
+  for (int s = 0; s < NM; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int8_t* q8 = &sm.qc[n < R ? n : 0][g * (D / 4) + 8 * (2 * s + e / 2) + (e & 1)];
+      qa[s][e] = n < R ? pack4_i8(q8[0], q8[2], q8[4], q8[6]) : 0;
+    }
+  int corr[4], Lr[4];
+  float cq[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = 4 * g + r;
+    corr[r] = rr < R ? 8 * sm.sumq[rr] : 0;
+    cq[r] = rr < R ? sm.cq[rr] : 0.f;
+    Lr[r] = rr < R ? row_len<G>(p, sl, rr) : 0;
+  }
+
+  constexpr int kChunk = 4;
+  for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
+    u32x4_t cw[kChunk][4];
+    float sc[kChunk][4];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int jl = jc + c * kWaves;
+      if (jl < nblk) {
+        const int jb = jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split];
+        const int t0 = jb * kBlockSize;
+        const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
+        const uint8_t* kq = p.kq + r0 * (D / 2);
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          const int t = t0 + 16 * T + n;
+          const bool ok = t < L;
+          const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * (D / 2) + g * (D / 8);
+          if constexpr (D == 128) {
+            cw[c][T] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
+          } else {
+            const u32x2_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{0u, 0u};
+            cw[c][T] = u32x4_t{u.x, u.y, 0u, 0u};
+          }
+          sc[c][T] = ok ? __builtin_nontemporal_load(p.kscale + r0 + (t - t0)) : 0.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int jl = jc + c * kWaves;
+      if (jl >= nblk) continue;
+      const int t0 = (jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split]) * kBlockSize;
+      float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        i32x4_t acc = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < NM; ++s) {
+          const uint32_t x0 = cw[c][T][2 * s] ^ 0x88888888u;   // two's complement -> code + 8
+          const uint32_t x1 = cw[c][T][2 * s + 1] ^ 0x88888888u;
+          const i32x4_t kb = i32x4_t{(int)(x0 & 0x0f0f0f0fu), (int)((x0 >> 4) & 0x0f0f0f0fu),
+                                     (int)(x1 & 0x0f0f0f0fu), (int)((x1 >> 4) & 0x0f0f0f0fu)};
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[s], kb, acc, 0, 0, 0);
+        }
+        const int t = t0 + 16 * T + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float wgt = sc[c][T] * cq[r];
+          const float sv = (float)(acc[r] - corr[r]) * wgt;
+          if (t < Lr[r]) bm[r] = fmaxf(bm[r], sv);
+        }
+      }
+      // max over the 16 token columns of each row (one DPP row of 16 lanes)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = bm[r];
+        m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
+        m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
+        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+        m = fmaxf(m, dpp_f<kDppMirror>(m));
+        bm[r] = m;
+      }
+      if (n == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = 4 * g + r;
+          if (rr < R) {
+            if (jl < nblk_split) sm.blk[jl][rr] = bm[r];
+            else sm.xblk[jl - nblk_split][rr] = bm[r];
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // select: split-local Top-δ ([TS] Methodology 2, "Mechanism" and
 // "Pseudo-Max Approximation"; sink and local blocks always kept)
 // ---------------------------------------------------------------------------
-template <int D, int G, bool DENSE>
-__device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j,
-                                              int j0, int nblk, int nmask, int NB, int lane) {
+// Row r (query token r / G, head r % G) sees NB_r blocks; a block it cannot see
+// is never kept for it, and its sink/local blocks are those of its own range.
+template <int D, int G, int QT, bool DENSE>
+__device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
+                                              int j0, int nblk, int nmask, int sl, int lane) {
+  constexpr int R = G * QT;
   const int jl = lane;
   const int jb = j0 + jl;
   const bool in_split = jl < nblk;
   unsigned hm = 0;
-  if constexpr (DENSE) {
-    hm = in_split ? ((1u << G) - 1u) : 0u;
-  } else {
-    float s[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = in_split ? sm.blk[jl][h] : -INFINITY;
-    const bool forced = jb < p.sink || jb >= NB - p.local;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mt = wave_max_f(s[h]);   // split max: the pseudo-max in split mode, else the seed
-      const float pm = p.pm_sink_local ? sm.pm[h] : mt;
+  for (int r = 0; r < R; ++r) {
+    const int NBr = (row_len<G>(p, sl, r) + kBlockSize - 1) / kBlockSize;
+    const bool vis = in_split && jb < NBr;
+    if constexpr (DENSE) {
+      if (vis) hm |= 1u << r;
+    } else {
+      const float s = vis ? sm.blk[jl][r] : -INFINITY;
+      const bool forced = jb < p.sink || jb >= NBr - p.local;
+      const float mt = wave_max_f(s);   // split max: the pseudo-max in split mode, else the seed
+      const float pm = p.pm_sink_local ? sm.pm[r] : mt;
       const float thr = pm - p.delta;
-      if (in_split && (s[h] >= thr || forced)) hm |= 1u << h;
-      if (lane == 0) sm.seed[h] = mt;
+      if (vis && (s >= thr || forced)) hm |= 1u << r;
+      if (lane == 0) sm.seed[r] = mt;
     }
   }
   if (p.mask != nullptr && jl < nmask) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      p.mask[((size_t)b * p.Hq + (size_t)j * G + h) * p.nb_max + jb] = (uint8_t)((hm >> h) & 1u);
+    for (int r = 0; r < R; ++r)
+      if (r / G < p.Q) p.mask[row_index<G>(p, b, j, r) * p.nb_max + jb] = (uint8_t)((hm >> r) & 1u);
   }
   const unsigned long long bal = __ballot(hm != 0u);
   const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
   if (hm != 0u) {
     sm.kidx[pos] = (uint8_t)jl;
-    sm.khm[pos] = (uint8_t)hm;
+    sm.khm[pos] = (uint16_t)hm;
   }
   if (lane == 0) sm.nkept = __popcll(bal);
 }
@@ -409,9 +546,12 @@ struct AttendState {
   float l;   // this lane's share of the normaliser
 };
 
-template <int D, int G, bool DENSE, bool THUMB>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
-                                              int L, int lane, int w, AttendState<D>& st) {
+// Lrow: tokens this lane's row (lane % 16) may see; L: tokens of the sequence
+// (the longest row), which bounds every load.
+template <int D, int G, int QT, bool DENSE, bool THUMB>
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
+                                              int j0, int L, int Lrow, int lane, int w, AttendState<D>& st) {
+  constexpr int R = G * QT;
   constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
   constexpr int NT = D / 16;    // MFMA n-tiles of the output
   constexpr int VC = D / 8;     // 16-byte chunks per V row
@@ -419,20 +559,21 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   const int h = lane & 15;
   const int g = lane >> 4;
 
-  // B operand of QK: the bf16 query of head h, dims g*D/4 + 8s .. +8 for k-step s
+  const bool hv = h < R && h / G < p.Q;   // a row of a real query token
+  // B operand of QK: the bf16 query of row h, dims g*D/4 + 8s .. +8 for k-step s
   bf16x8_t qop[KS];
   {
-    const uint16_t* qh = p.q + ((size_t)b * p.Hq + (size_t)j * G + (h < G ? h : 0)) * D + g * (D / 4);
+    const uint16_t* qh = p.q + row_index<G>(p, b, j, hv ? h : 0) * D + g * (D / 4);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4_t u = u32x4_t{0u, 0u, 0u, 0u};
-      if (h < G) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
+      if (hv) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
       qop[s] = as_bf16x8(u);
     }
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) st.o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = (h < G) ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
+  st.m = hv ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
   st.l = 0.f;
 
   char* vt = reinterpret_cast<char*>(sm.vt[w]);
@@ -538,7 +679,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
           au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_u, qop[s], au, 0, 0, 0);
           ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_r, qop[s], ar, 0, 0, 0);
         }
-        const float qs = (h < G) ? sm.qsumf[h] : 0.f;
+        const float qs = hv ? sm.qsumf[h] : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int src = 16 * T + 4 * g + r;   // the lane holding this row's scales
@@ -565,7 +706,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       *reinterpret_cast<u32x4_t*>(vt + wbase[n & 1] + (n >> 1) * 2048) = vr[n];
 
     // ---- online softmax in the MFMA output layout ----
-    const bool head_keeps = (h < G) && ((hm >> h) & 1u);
+    const bool head_keeps = hv && ((hm >> h) & 1u);
     float sv[4][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -574,7 +715,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + 16 * T + 4 * g + r;
         const float z = sacc[T][r] * zscale;
-        sv[T][r] = (head_keeps && t < L) ? z : -INFINITY;
+        sv[T][r] = (head_keeps && t < Lrow) ? z : -INFINITY;
         mx = fmaxf(mx, sv[T][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -649,38 +790,48 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, flo
   else static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(v);
 }
 
-template <int D, int G, bool DENSE, bool THUMB>
+// One workgroup per (split, kv head j, sequence b) serving R = G x QT query
+// rows: the G heads of the group for each of the (up to QT) query tokens.
+template <int D, int G, int QT, bool DENSE, bool THUMB>
 __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodeParams p) {
-  __shared__ DecodeSmem<D, G> sm;
+  constexpr int R = G * QT;
+  static_assert(QT == 1 || !THUMB, "several query tokens only with the int4 sketch");
+  __shared__ DecodeSmem<D, R> sm;
   const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  const int sl = p.seq_lens[b];
+  // the last query token sees the whole sequence: every load is bounded by it
+  const int L = row_len<G>(p, sl, G * (p.Q - 1));
   const int NB = (L + kBlockSize - 1) / kBlockSize;
   const int j0 = split * p.split_blocks;
   const int nmask = min(p.split_blocks, p.nb_max - j0);
   if (j0 >= NB) {
     // no valid block in this split: only the mask entries are owned here
     if (p.mask != nullptr) {
-      for (int i = tid; i < nmask * G; i += kThreads) {
-        const int h = i / nmask, jl = i % nmask;
-        p.mask[((size_t)b * p.Hq + (size_t)j * G + h) * p.nb_max + j0 + jl] = 0;
+      for (int i = tid; i < nmask * R; i += kThreads) {
+        const int r = i / nmask, jl = i % nmask;
+        if (r / G < p.Q) p.mask[row_index<G>(p, b, j, r) * p.nb_max + j0 + jl] = 0;
       }
     }
     return;
   }
   const int nblk = min(p.split_blocks, NB - j0);
 
-  // ---- prologue: query to LDS, int8 scan query --------------------------
-  const uint16_t* qg = p.q + ((size_t)b * p.Hq + (size_t)j * G) * D;
-  for (int i = tid; i < G * D; i += kThreads) sm.q[i / D][i % D] = bf16_to_f32(qg[i]);
+  // ---- prologue: query rows to LDS, int8 scan query -----------------------
+  for (int i = tid; i < R * D; i += kThreads) {
+    const int r = i / D;
+    sm.q[r][i % D] = (r / G < p.Q) ? bf16_to_f32(p.q[row_index<G>(p, b, j, r) * D + i % D]) : 0.f;
+  }
   if (p.block_table != nullptr && tid < nblk)
     sm.rowp[tid] = (int)(cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, j0 + tid) /
                          kBlockSize);
   if (!DENSE && p.pm_sink_local && tid == 0) {
+    // sink and local blocks of every row that lie outside the split: the rows'
+    // local windows end at NB_0 .. NB (first to last query token)
+    const int NB0 = (row_len<G>(p, sl, 0) + kBlockSize - 1) / kBlockSize;
     int nx = 0;
     const int s_end = min(p.sink, NB);
-    const int l_beg = max(s_end, NB - p.local);
+    const int l_beg = max(s_end, NB0 - p.local);
     for (int jb = 0; jb < s_end; ++jb)
       if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
     for (int jb = l_beg; jb < NB; ++jb)
@@ -688,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     sm.nx = nx;
   }
   __syncthreads();
-  for (int h = w; h < G; h += kWaves) {
+  for (int h = w; h < R; h += kWaves) {
     constexpr int PER = D / kWave;
     float x[PER];
     float amax = 0.f;
@@ -737,28 +888,33 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     // sink/local pseudo-max: the sink and local blocks outside this split are
     // listed in the prologue and scanned in the same pass as the split
     const int nx = p.pm_sink_local ? sm.nx : 0;
-    if constexpr (THUMB) scan_blocks_thumb<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
+    if constexpr (QT > 1) scan_blocks_mq<D, G, QT>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
+    else if constexpr (THUMB) scan_blocks_thumb<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
     else scan_blocks<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
     __syncthreads();
-    if (p.pm_sink_local && tid < G) {
+    if (p.pm_sink_local && tid < R) {
+      const int NBr = (row_len<G>(p, sl, tid) + kBlockSize - 1) / kBlockSize;
       float m = -INFINITY;
-      for (int x = 0; x < nx; ++x) m = fmaxf(m, sm.xblk[x][tid]);
+      for (int x = 0; x < nx; ++x) {
+        const int jb = sm.xidx[x];
+        if (jb < NBr && (jb < p.sink || jb >= NBr - p.local)) m = fmaxf(m, sm.xblk[x][tid]);
+      }
       for (int jl = 0; jl < nblk; ++jl) {
         const int jb = j0 + jl;
-        if (jb < p.sink || jb >= NB - p.local) m = fmaxf(m, sm.blk[jl][tid]);
+        if (jb < NBr && (jb < p.sink || jb >= NBr - p.local)) m = fmaxf(m, sm.blk[jl][tid]);
       }
       sm.pm[tid] = m;
     }
     if (p.pm_sink_local) __syncthreads();
   }
-  if (w == 0) select_blocks<D, G, DENSE>(p, sm, b, j, j0, nblk, nmask, NB, lane);
+  if (w == 0) select_blocks<D, G, QT, DENSE>(p, sm, b, j, j0, nblk, nmask, sl, lane);
   __syncthreads();
 
   // ---- attend -------------------------------------------------------------
   AttendState<D> st;
-  attend_blocks<D, G, DENSE, THUMB>(p, sm, b, j, j0, L, lane, w, st);
+  attend_blocks<D, G, QT, DENSE, THUMB>(p, sm, b, j, j0, L, row_len<G>(p, sl, lane & 15), lane, w, st);
 
-  // this wave's partial: normaliser of head h summed over its 4 lane groups;
+  // this wave's partial: normaliser of row h summed over its 4 lane groups;
   // the partial outputs overwrite the V tiles, so every wave must be done
   __syncthreads();
   float lw = st.l;
@@ -769,12 +925,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int hh = 4 * g + r;
-      if (hh < G) {
+      if (hh < R) {
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) sm.wo[w][hh][16 * nt + (lane & 15)] = st.o[nt][r];
       }
     }
-    if (lane < G) {
+    if (lane < R) {
       sm.wm[w][lane] = st.m;
       sm.wl[w][lane] = lw;
     }
@@ -782,8 +938,9 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   __syncthreads();
 
   // ---- epilogue: merge waves, write the split partial -------------------
-  for (int i = tid; i < G * D; i += kThreads) {
+  for (int i = tid; i < R * D; i += kThreads) {
     const int h = i / D, cc = i % D;
+    if (h / G >= p.Q) continue;
     float mx = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, sm.wm[ww][h]);
@@ -794,12 +951,12 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
       den += sm.wl[ww][h] * a;
       num += sm.wo[ww][h][cc] * a;
     }
-    const size_t row = ((size_t)b * p.Hq + (size_t)j * G + h) * p.n_splits + split;
-    // a split can keep no block of a head (sink/local pseudo-max): empty partial
+    const size_t row = row_index<G>(p, b, j, h) * p.n_splits + split;
+    // a row can keep no block of a split (sink/local pseudo-max, or a query
+    // token that does not see the split): empty partial
     p.o_part[row * D + cc] = den > 0.f ? num / den : 0.f;
     if (cc == 0) p.lse_part[row] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
   }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -818,7 +975,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
   L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
   const int NB = (L + kBlockSize - 1) / kBlockSize;
   const int ns = (NB + p.split_blocks - 1) / p.split_blocks;
-  const size_t bh = (size_t)b * p.Hq + h;
+  const size_t bh = (size_t)b * p.Q * p.Hq + h;   // row (b, query token h / Hq, head h % Hq)
   const float* lp = p.lse_part + bh * p.n_splits;
   const float* op = p.o_part + bh * p.n_splits * D;
   if (tid < kWave) {
@@ -848,25 +1005,47 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
   }
 }
 
-template <int D, int G, bool DENSE, bool THUMB>
+template <int D, int G, int QT, bool DENSE, bool THUMB>
 hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) {
   if ((static_cast<int>(stage) & static_cast<int>(Stage::kPartials)) && p.n_splits > 0) {
     dim3 grid(p.n_splits, p.Hkv, p.B);
-    fused_decode_kernel<D, G, DENSE, THUMB><<<grid, kThreads, 0, stream>>>(p);
+    fused_decode_kernel<D, G, QT, DENSE, THUMB><<<grid, kThreads, 0, stream>>>(p);
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
-    combine_kernel<D><<<dim3(p.Hq, p.B), 512, 0, stream>>>(p);
+    combine_kernel<D><<<dim3(p.Q * p.Hq, p.B), 512, 0, stream>>>(p);
   }
   return hipGetLastError();
+}
+
+// Query tokens per workgroup: the smallest power of two >= Q (rows of the
+// missing tokens are padding); G * QT <= 16.
+template <int D, int G, bool DENSE, bool THUMB>
+hipError_t launch_q(const DecodeParams& p, Stage stage, hipStream_t stream) {
+  if (p.Q == 1) return launch_fused<D, G, 1, DENSE, THUMB>(p, stage, stream);
+  if constexpr (THUMB) {
+    return hipErrorInvalidValue;
+  } else {
+    if (p.Q <= 2) return launch_fused<D, G, 2, DENSE, false>(p, stage, stream);
+    if constexpr (G <= 4) {
+      if (p.Q <= 4) return launch_fused<D, G, 4, DENSE, false>(p, stage, stream);
+    }
+    if constexpr (G <= 2) {
+      if (p.Q <= 8) return launch_fused<D, G, 8, DENSE, false>(p, stage, stream);
+    }
+    if constexpr (G == 1) {
+      if (p.Q <= 16) return launch_fused<D, G, 16, DENSE, false>(p, stage, stream);
+    }
+    return hipErrorInvalidValue;
+  }
 }
 
 template <int D, bool DENSE, bool THUMB>
 hipError_t launch_g(const DecodeParams& p, int G, Stage stage, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_fused<D, 1, DENSE, THUMB>(p, stage, stream);
-    case 2: return launch_fused<D, 2, DENSE, THUMB>(p, stage, stream);
-    case 4: return launch_fused<D, 4, DENSE, THUMB>(p, stage, stream);
-    case 8: return launch_fused<D, 8, DENSE, THUMB>(p, stage, stream);
+    case 1: return launch_q<D, 1, DENSE, THUMB>(p, stage, stream);
+    case 2: return launch_q<D, 2, DENSE, THUMB>(p, stage, stream);
+    case 4: return launch_q<D, 4, DENSE, THUMB>(p, stage, stream);
+    case 8: return launch_q<D, 8, DENSE, THUMB>(p, stage, stream);
     default: return hipErrorInvalidValue;
   }
 }

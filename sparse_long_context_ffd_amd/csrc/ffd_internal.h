@@ -10,10 +10,13 @@ namespace ffd {
 constexpr int kBlockSize = 64;   // tokens per selection block
 constexpr int kMaxSplit = 64;    // max blocks per split (one workgroup)
 constexpr int kMaxPseudoMax = 64; // max sink + local blocks with the sink/local pseudo-max
+constexpr int kMaxRows = 16;     // query rows (query tokens x heads of a kv group) per workgroup
 constexpr size_t kWsAlign = 256;
 
+// Q query tokens per sequence (Q = 1: ordinary decode). Query-head rows are
+// indexed (b * Q + i) * Hq + h throughout: q, out, lse, mask and partials.
 struct DecodeParams {
-  const uint16_t* q;       // bf16 [B, Hq, D]
+  const uint16_t* q;       // bf16 [B, Q, Hq, D]
   const uint16_t* k;       // bf16 [B, Hkv, cap, D]
   const uint16_t* v;       // bf16 [B, Hkv, cap, D]
   const uint8_t* kq;       // u8   [B, Hkv, cap, D/2]
@@ -25,13 +28,13 @@ struct DecodeParams {
   const int32_t* seq_lens; // [B]
   const int32_t* block_table;  // [B, table_stride] page of each block, or null (contiguous cache)
   int table_stride, num_pages; // paged cache: K/V [num_pages, Hkv, 64, D], kq/kscale alike
-  float* o_part;           // f32  [B, Hq, n_splits, D]   (normalised per split)
-  float* lse_part;         // f32  [B, Hq, n_splits]      (natural log)
-  uint8_t* mask;           // u8   [B, Hq, nb_max] or null
-  void* out;               // bf16 / f32 [B, Hq, D]
-  float* lse;              // f32 [B, Hq]
+  float* o_part;           // f32  [B, Q, Hq, n_splits, D]   (normalised per split)
+  float* lse_part;         // f32  [B, Q, Hq, n_splits]      (natural log)
+  uint8_t* mask;           // u8   [B, Q, Hq, nb_max] or null
+  void* out;               // bf16 / f32 [B, Q, Hq, D]
+  float* lse;              // f32 [B, Q, Hq]
   int out_f32;
-  int max_seq_len, B, Hq, Hkv, cap;
+  int max_seq_len, B, Q, Hq, Hkv, cap;
   int nb_max;              // ceil(max_seq_len / kBlockSize)
   int n_splits;            // ceil(nb_max / split_blocks)
   int split_blocks;
@@ -61,8 +64,9 @@ hipError_t launch_quantize_thumb(const uint16_t* k, uint8_t* k2, float* k2scale,
 
 enum class Stage { kPartials = 1, kCombine = 2, kBoth = 3 };
 
-// Returns hipErrorInvalidValue for an unsupported (D, G) pair. thumb: K comes
-// from the thumbnail + residual storage instead of bf16 K and the int4 sketch.
+// Returns hipErrorInvalidValue for an unsupported (D, G, p.Q) combination
+// (G * Q <= 16; Q > 1 only with the int4 storage). thumb: K comes from the
+// thumbnail + residual storage instead of bf16 K and the int4 sketch.
 hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream,
                          bool thumb = false);
 

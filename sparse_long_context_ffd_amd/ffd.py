@@ -34,7 +34,8 @@ PSEUDO_MAX = {"split": 0, "sink_local": 1}
 
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_quantize_kv_paged",
                     "ffd_quantize_kv_thumb", "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged",
-                    "ffd_decode_thumb", "ffd_decode_partials", "ffd_combine")
+                    "ffd_decode_thumb", "ffd_decode_partials", "ffd_combine", "ffd_decode_multi",
+                    "ffd_decode_multi_workspace_bytes")
 
 
 class FFDError(RuntimeError):
@@ -73,6 +74,15 @@ def lib() -> ctypes.CDLL:
                              ctypes.c_float,                        # sm_scale
                              _vp, _i, _vp, _vp,                     # out out_dtype lse mask
                              _vp, ctypes.c_size_t, _vp]             # workspace bytes stream
+    L.ffd_decode_multi.restype = _i
+    L.ffd_decode_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,        # q k v kq kscale seq_lens
+                                   _i, _i, _i, _i, _i, _i, _i,          # max_seq_len B Q Hq Hkv d cap
+                                   _i, ctypes.c_float, _i, _i, _i, _i,  # block_size delta sink local pm split
+                                   ctypes.c_float,                      # sm_scale
+                                   _vp, _i, _vp, _vp,                   # out out_dtype lse mask
+                                   _vp, ctypes.c_size_t, _vp]           # workspace bytes stream
+    L.ffd_decode_multi_workspace_bytes.restype = ctypes.c_size_t
+    L.ffd_decode_multi_workspace_bytes.argtypes = [_i] * 7
     L.ffd_decode_partials.restype = _i
     L.ffd_decode_partials.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                       _i, ctypes.c_float, _i, _i, _i, _i, ctypes.c_float,
@@ -206,6 +216,35 @@ def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[t
                             int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out), odt,
                             _ptr(lse),
                             _ptr(kept_mask), _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def ffd_decode_multi_workspace_bytes(B: int, Q: int, Hq: int, d: int, max_seq_len: int, block_size: int = 64,
+                                     split_blocks: int = 32) -> int:
+    return int(lib().ffd_decode_multi_workspace_bytes(B, Q, Hq, d, max_seq_len, block_size, split_blocks))
+
+
+def ffd_decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[torch.Tensor],
+                     kscale: Optional[torch.Tensor], seq_lens: torch.Tensor, *, max_seq_len: int, block_size: int,
+                     delta: float, sink: int, local: int, split_blocks: int, sm_scale: float, out: torch.Tensor,
+                     lse: torch.Tensor, kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
+                     pseudo_max: str = "split", stream=None) -> None:
+    """Q query tokens per sequence (``q`` ``[B, Q, Hq, d]``; token i sees the
+    cache up to position ``seq_lens[b] - Q + i``) into preallocated ``out``
+    ``[B, Q, Hq, d]`` / ``lse`` ``[B, Q, Hq]`` / ``kept_mask`` ``[B, Q, Hq, NB]``."""
+    _need(q, "q", torch.bfloat16, 4)
+    B, Q, Hq, d = q.shape
+    flat = q.view(B, Q * Hq, d)
+    mflat = None if kept_mask is None else kept_mask.view(B, Q * Hq, kept_mask.shape[-1])
+    _, _, Hkv, _, cap = _check_decode_inputs(flat, k, v, kq, kscale, seq_lens, max_seq_len, block_size, mflat)
+    if tuple(out.shape[:3]) != (B, Q, Hq) or tuple(lse.shape) != (B, Q, Hq):
+        raise ValueError("out/lse shapes")
+    if kept_mask is not None and tuple(kept_mask.shape[:3]) != (B, Q, Hq):
+        raise ValueError("kept_mask shape")
+    odt = _check_outputs(out.view(B, Q * Hq, out.shape[-1]), lse.view(B, Q * Hq), B, Q * Hq, d)
+    _check(lib().ffd_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
+                                  int(max_seq_len), B, Q, Hq, Hkv, d, cap, int(block_size), float(delta), int(sink),
+                                  int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out), odt,
+                                  _ptr(lse), _ptr(kept_mask), _ptr(workspace), _ws(workspace), _stream(stream)))
 
 
 def ffd_decode_partials(q, k, v, kq, kscale, seq_lens, *, max_seq_len: int, block_size: int, delta: float,
@@ -383,4 +422,28 @@ def decode(q, k, v, kq, kscale, seq_lens, *, max_seq_len: Optional[int] = None, 
     ffd_decode(q, k, v, kq, kscale, seq_lens, max_seq_len=max_seq_len, block_size=block_size, delta=delta,
                sink=sink, local=local, split_blocks=split_blocks, sm_scale=sm_scale, out=out, lse=lse,
                kept_mask=mask, workspace=workspace, pseudo_max=pseudo_max, stream=stream)
+    return out, lse, mask
+
+
+def decode_multi(q, k, v, kq, kscale, seq_lens, *, max_seq_len: Optional[int] = None, block_size: int = 64,
+                 delta: float = 6.0, sink: int = 1, local: int = 4, split_blocks: int = 32,
+                 sm_scale: Optional[float] = None, out_dtype=torch.bfloat16, with_mask: bool = True,
+                 workspace: Optional[torch.Tensor] = None, pseudo_max: str = "split", stream=None):
+    """Allocate outputs and run one multi-query step (``q`` ``[B, Q, Hq, d]``);
+    returns ``(out, lse, kept_mask)``."""
+    B, Q, Hq, d = q.shape
+    if max_seq_len is None:
+        max_seq_len = k.shape[2]
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    out = torch.empty((B, Q, Hq, d), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, Q, Hq), dtype=torch.float32, device=q.device)
+    nb_max = -(-max_seq_len // block_size)
+    mask = torch.empty((B, Q, Hq, nb_max), dtype=torch.uint8, device=q.device) if with_mask else None
+    if workspace is None:
+        n = ffd_decode_multi_workspace_bytes(B, Q, Hq, d, max_seq_len, block_size, split_blocks)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    ffd_decode_multi(q, k, v, kq, kscale, seq_lens, max_seq_len=max_seq_len, block_size=block_size, delta=delta,
+                     sink=sink, local=local, split_blocks=split_blocks, sm_scale=sm_scale, out=out, lse=lse,
+                     kept_mask=mask, workspace=workspace, pseudo_max=pseudo_max, stream=stream)
     return out, lse, mask

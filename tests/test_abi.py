@@ -118,3 +118,45 @@ def test_paged_validation():
     assert st == ffd.FFD_ERR_INVALID_ARG and "num_pages" in ffd.ffd_last_error()
     st = L.ffd_quantize_kv_paged(fake, fake, fake, None, 4, 10, fake, fake, 1, 8, 128, 64, None)
     assert st == ffd.FFD_ERR_INVALID_ARG and "block_table" in ffd.ffd_last_error()
+
+
+def _decode_multi(**kw):
+    args = dict(q=None, k=None, v=None, kq=None, kscale=None, seq_lens=None, max_seq_len=128, B=1, Q=2, Hq=4, Hkv=1,
+                d=128, cap=128, block_size=64, delta=6.0, sink=1, local=4, pm=0, split=32, sm_scale=0.088388,
+                out=None, out_dtype=0, lse=None, mask=None, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    L = ffd.lib()
+    return L.ffd_decode_multi(args["q"], args["k"], args["v"], args["kq"], args["kscale"], args["seq_lens"],
+                              args["max_seq_len"], args["B"], args["Q"], args["Hq"], args["Hkv"], args["d"],
+                              args["cap"], args["block_size"], ctypes.c_float(args["delta"]), args["sink"],
+                              args["local"], args["pm"], args["split"], ctypes.c_float(args["sm_scale"]), args["out"],
+                              args["out_dtype"], args["lse"], args["mask"], args["ws"], args["ws_bytes"],
+                              args["stream"])
+
+
+def test_multi_workspace_bytes():
+    for B, Q, Hq in ((4, 4, 32), (1, 16, 8), (2, 1, 32)):
+        assert ffd.ffd_decode_multi_workspace_bytes(B, Q, Hq, 128, 131072, 64, 32) == \
+            ffd.ffd_decode_workspace_bytes(B, Q * Hq, 128, 131072, 64, 32)
+    assert ffd.ffd_decode_multi_workspace_bytes(4, 0, 32, 128, 131072, 64, 32) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(Q=0), ffd.FFD_ERR_INVALID_ARG, "Q=0"),
+    (dict(Q=5, Hq=4, Hkv=1), ffd.FFD_ERR_UNSUPPORTED, "rows per workgroup"),
+    (dict(Q=3, Hq=8, Hkv=1), ffd.FFD_ERR_UNSUPPORTED, "rows per workgroup"),
+    (dict(Q=16, Hq=2, Hkv=2, pm=1, sink=32, local=32), ffd.FFD_ERR_UNSUPPORTED, "exceeds"),
+    (dict(Q=2), ffd.FFD_ERR_INVALID_ARG, "null"),
+])
+def test_multi_host_validation(kw, status, needle):
+    assert _decode_multi(**kw) == status
+    assert needle in ffd.ffd_last_error()
+
+
+def test_multi_workspace_covers_every_query_row():
+    fake = 1 << 20  # never dereferenced: validation fails before any launch
+    common = dict(q=fake, k=fake, v=fake, kq=fake, kscale=fake, seq_lens=fake, out=fake, lse=fake, ws=fake)
+    one = ffd.ffd_decode_workspace_bytes(1, 4, 128, 128, 64, 32)
+    assert _decode_multi(**common, ws_bytes=one, Q=2) == ffd.FFD_ERR_WORKSPACE
+    assert _decode_multi(**common, ws_bytes=one, Q=4, pm=1, sink=0, local=0) == ffd.FFD_ERR_INVALID_ARG
+    assert _decode_multi(B=0, Q=4) == ffd.FFD_OK
