@@ -249,7 +249,11 @@ def main() -> int:
     lse = torch.empty((B,) + rows + (w.Hq,), dtype=torch.float32, device=dev)
     nb_max = -(-msl // w.block_size)
     mask = torch.empty((B,) + rows + (w.Hq, nb_max), dtype=torch.uint8, device=dev)
-    ws = ffd.alloc_workspace(B, Q * w.Hq, d, msl, w.block_size, w.split_blocks, dev)
+    if Q > 1:
+        ws = torch.empty(ffd.ffd_decode_multi_workspace_bytes(B, Q, w.Hq, d, msl, w.block_size, w.split_blocks),
+                         dtype=torch.uint8, device=dev)
+    else:
+        ws = ffd.alloc_workspace(B, w.Hq, d, msl, w.block_size, w.split_blocks, dev)
     kw = dict(max_seq_len=msl, block_size=w.block_size, split_blocks=w.split_blocks)
 
     if args.paged:

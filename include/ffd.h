@@ -274,12 +274,17 @@ ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2sca
  * Top-δ select -> attend kernel, one workgroup per (sequence, kv head,
  * split) ([TS] Methodology 3, "Fused Kernel"). Same arguments and semantics
  * as ffd_decode (the kept_mask is written here); instead of the final output
- * it leaves every split's partial result in the workspace:
+ * it leaves every split's partial results in the workspace:
  *   n_splits = ceil(ceil(max_seq_len / block_size) / split_blocks)
- *   o_part   f32 [B, Hq, n_splits, d] at byte offset 0: the split's
- *            attention output, normalised over the split's kept tokens
- *   lse_part f32 [B, Hq, n_splits] at byte offset
- *            round_up(B*Hq*n_splits*d*4, 256): natural-log normaliser
+ *   P        = clamp(floor(2048 / (B * Hq * n_splits)), 1, 4): workgroups
+ *              per split when the grid alone would leave the chip idle;
+ *              each scans and selects the whole split (one kept set) and
+ *              attends every P-th kept block
+ *   o_part   f32 [B, Hq, n_splits, P, d] at byte offset 0: each part's
+ *            attention output, normalised over the kept tokens it attended
+ *   lse_part f32 [B, Hq, n_splits, P] at byte offset
+ *            round_up(B*Hq*n_splits*P*d*4, 256): natural-log normaliser
+ *            (-INFINITY for a part that attended nothing)
  * Only splits s < ceil(NB_b / split_blocks) of sequence b are written.
  * Combining the partials of disjoint token sets by log-sum-exp is exact,
  * which is what lets a sequence be split across workgroups (and, by the

@@ -35,6 +35,14 @@ int n_splits_for(int max_seq_len, int split_blocks) {
   return (nb_max + split_blocks - 1) / split_blocks;
 }
 
+// Workspace of a decode over B sequences with `rows` query-head rows each
+// (Hq, or Q * Hq), Hq query heads per token: one partial per row, split and part.
+size_t decode_ws_bytes(int B, int rows, int Hq, int max_seq_len, int split_blocks, int d) {
+  const int ns = n_splits_for(max_seq_len, split_blocks);
+  const int np = ns * ffd::split_parts_for(B, Hq, ns);
+  return ffd::ws_opart_bytes(B, rows, np, d) + ffd::ws_lse_bytes(B, rows, np);
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,13 +124,13 @@ ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* 
 size_t ffd_decode_multi_workspace_bytes(int B, int Q, int Hq, int d, int max_seq_len, int block_size,
                                         int split_blocks) {
   if (Q <= 0 || Hq <= 0 || (long)Q * Hq > 65535) return 0;
-  return ffd_decode_workspace_bytes(B, Q * Hq, d, max_seq_len, block_size, split_blocks);
+  if (B <= 0 || d <= 0 || max_seq_len <= 0 || block_size != ffd::kBlockSize || split_blocks < 1) return 0;
+  return decode_ws_bytes(B, Q * Hq, Hq, max_seq_len, split_blocks, d);
 }
 
 size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int block_size, int split_blocks) {
   if (B <= 0 || Hq <= 0 || d <= 0 || max_seq_len <= 0 || block_size != ffd::kBlockSize || split_blocks < 1) return 0;
-  const int ns = n_splits_for(max_seq_len, split_blocks);
-  return ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns);
+  return decode_ws_bytes(B, Hq, Hq, max_seq_len, split_blocks, d);
 }
 
 }  // extern "C"
@@ -191,8 +199,10 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   const int nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
   const int rows = Q * Hq;   // query-head rows per sequence
-  const size_t need =
-      (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, rows, ns, d) + ffd::ws_lse_bytes(B, rows, ns) : 0;
+  const int parts = ns > 0 ? ffd::split_parts_for(B, Hq, ns) : 1;
+  const size_t need = (B > 0 && max_seq_len > 0)
+                          ? ffd::ws_opart_bytes(B, rows, ns * parts, d) + ffd::ws_lse_bytes(B, rows, ns * parts)
+                          : 0;
   if (need > 0) {
     if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);
     if (workspace_bytes < need)
@@ -212,7 +222,7 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.num_pages = num_pages;
   char* ws = static_cast<char*>(workspace);
   p.o_part = need ? reinterpret_cast<float*>(ws) : nullptr;
-  p.lse_part = need ? reinterpret_cast<float*>(ws + ffd::ws_opart_bytes(B, rows, ns, d)) : nullptr;
+  p.lse_part = need ? reinterpret_cast<float*>(ws + ffd::ws_opart_bytes(B, rows, ns * parts, d)) : nullptr;
   p.mask = kept_mask;
   p.max_seq_len = max_seq_len;
   p.B = B;
@@ -222,6 +232,7 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.cap = cap;
   p.nb_max = nb_max;
   p.n_splits = ns;
+  p.split_parts = parts;
   p.split_blocks = split_blocks;
   p.sink = sink_blocks;
   p.local = local_blocks;
@@ -398,7 +409,10 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   if (st != FFD_OK) return st;
   if (B > 0 && !seq_lens) return fail(FFD_ERR_INVALID_ARG, "%s: null seq_lens", fn);
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
-  const size_t need = (B > 0 && max_seq_len > 0) ? ffd::ws_opart_bytes(B, Hq, ns, d) + ffd::ws_lse_bytes(B, Hq, ns) : 0;
+  const int parts = ns > 0 ? ffd::split_parts_for(B, Hq, ns) : 1;
+  const size_t need = (B > 0 && max_seq_len > 0)
+                          ? ffd::ws_opart_bytes(B, Hq, ns * parts, d) + ffd::ws_lse_bytes(B, Hq, ns * parts)
+                          : 0;
   if (need > 0) {
     if (!workspace) return fail(FFD_ERR_INVALID_ARG, "%s: null workspace", fn);
     if (workspace_bytes < need)
@@ -409,7 +423,8 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   ffd::DecodeParams p{};
   const char* ws = static_cast<const char*>(workspace);
   p.o_part = need ? reinterpret_cast<float*>(const_cast<char*>(ws)) : nullptr;
-  p.lse_part = need ? reinterpret_cast<float*>(const_cast<char*>(ws) + ffd::ws_opart_bytes(B, Hq, ns, d)) : nullptr;
+  p.lse_part =
+      need ? reinterpret_cast<float*>(const_cast<char*>(ws) + ffd::ws_opart_bytes(B, Hq, ns * parts, d)) : nullptr;
   p.seq_lens = seq_lens;
   p.out = out;
   p.lse = lse;
@@ -421,6 +436,7 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   p.Hkv = 1;
   p.nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
   p.n_splits = ns;
+  p.split_parts = parts;
   p.split_blocks = split_blocks;
   return launch(fn, p, d, 1, false, ffd::Stage::kCombine, stream);
 }

@@ -548,9 +548,13 @@ struct AttendState {
 
 // Lrow: tokens this lane's row (lane % 16) may see; L: tokens of the sequence
 // (the longest row), which bounds every load.
+// Kept blocks first, first + stride, ... are this wave's; its V tile is the
+// one of wave w of the workgroup.
 template <int D, int G, int QT, bool DENSE, bool THUMB>
 __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
-                                              int j0, int L, int Lrow, int lane, int w, AttendState<D>& st) {
+                                              int j0, int L, int Lrow, int lane, int first, int stride,
+                                              AttendState<D>& st) {
+  const int w = first % kWaves;
   constexpr int R = G * QT;
   constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
   constexpr int NT = D / 16;    // MFMA n-tiles of the output
@@ -592,7 +596,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   const float zscale = p.sm_scale * kLog2e;
   const int nkept = sm.nkept;
 
-  for (int e = w; e < nkept; e += kWaves) {
+  for (int e = first; e < nkept; e += stride) {
     const int jb = j0 + sm.kidx[e];
     const unsigned hm = sm.khm[e];
     const int t0 = jb * kBlockSize;
@@ -797,7 +801,17 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   constexpr int R = G * QT;
   static_assert(QT == 1 || !THUMB, "several query tokens only with the int4 sketch");
   __shared__ DecodeSmem<D, R> sm;
-  const int split = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  const int j = blockIdx.y, b = blockIdx.z;
+  int split = blockIdx.x, part = 0;
+  if (p.split_parts > 1) {
+    // The P workgroups of a split get linear ids 8 apart (the x extent is a
+    // multiple of 8), which the dispatcher, dealing workgroups round-robin
+    // over the 8 XCDs, places on one XCD: their repeated scan reads share its L2.
+    const int x = blockIdx.x;
+    split = (x / (8 * p.split_parts)) * 8 + x % 8;
+    part = (x / 8) % p.split_parts;
+    if (split >= p.n_splits) return;
+  }
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const int sl = p.seq_lens[b];
   // the last query token sees the whole sequence: every load is bounded by it
@@ -807,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
   const int nmask = min(p.split_blocks, p.nb_max - j0);
   if (j0 >= NB) {
     // no valid block in this split: only the mask entries are owned here
-    if (p.mask != nullptr) {
+    if (p.mask != nullptr && part == 0) {
       for (int i = tid; i < nmask * R; i += kThreads) {
         const int r = i / nmask, jl = i % nmask;
         if (r / G < p.Q) p.mask[row_index<G>(p, b, j, r) * p.nb_max + j0 + jl] = 0;
@@ -907,12 +921,13 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
     }
     if (p.pm_sink_local) __syncthreads();
   }
-  if (w == 0) select_blocks<D, G, QT, DENSE>(p, sm, b, j, j0, nblk, nmask, sl, lane);
+  if (w == 0) select_blocks<D, G, QT, DENSE>(p, sm, b, j, j0, nblk, part == 0 ? nmask : 0, sl, lane);
   __syncthreads();
 
   // ---- attend -------------------------------------------------------------
   AttendState<D> st;
-  attend_blocks<D, G, QT, DENSE, THUMB>(p, sm, b, j, j0, L, row_len<G>(p, sl, lane & 15), lane, w, st);
+  attend_blocks<D, G, QT, DENSE, THUMB>(p, sm, b, j, j0, L, row_len<G>(p, sl, lane & 15), lane,
+                                        part * kWaves + w, kWaves * p.split_parts, st);
 
   // this wave's partial: normaliser of row h summed over its 4 lane groups;
   // the partial outputs overwrite the V tiles, so every wave must be done
@@ -951,7 +966,7 @@ __global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodePara
       den += sm.wl[ww][h] * a;
       num += sm.wo[ww][h][cc] * a;
     }
-    const size_t row = row_index<G>(p, b, j, h) * p.n_splits + split;
+    const size_t row = (row_index<G>(p, b, j, h) * p.n_splits + split) * p.split_parts + part;
     // a row can keep no block of a split (sink/local pseudo-max, or a query
     // token that does not see the split): empty partial
     p.o_part[row * D + cc] = den > 0.f ? num / den : 0.f;
@@ -974,10 +989,11 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
   const int NB = (L + kBlockSize - 1) / kBlockSize;
-  const int ns = (NB + p.split_blocks - 1) / p.split_blocks;
+  const int ns = (NB + p.split_blocks - 1) / p.split_blocks * p.split_parts;   // partials of this sequence
   const size_t bh = (size_t)b * p.Q * p.Hq + h;   // row (b, query token h / Hq, head h % Hq)
-  const float* lp = p.lse_part + bh * p.n_splits;
-  const float* op = p.o_part + bh * p.n_splits * D;
+  const size_t per_row = (size_t)p.n_splits * p.split_parts;
+  const float* lp = p.lse_part + bh * per_row;
+  const float* op = p.o_part + bh * per_row * D;
   if (tid < kWave) {
     const float l = merged_lse(lp, ns, tid);
     if (tid == 0) s_lse = l;
@@ -1008,7 +1024,8 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
 template <int D, int G, int QT, bool DENSE, bool THUMB>
 hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) {
   if ((static_cast<int>(stage) & static_cast<int>(Stage::kPartials)) && p.n_splits > 0) {
-    dim3 grid(p.n_splits, p.Hkv, p.B);
+    const int gx = p.split_parts == 1 ? p.n_splits : (p.n_splits + 7) / 8 * 8 * p.split_parts;
+    dim3 grid(gx, p.Hkv, p.B);
     fused_decode_kernel<D, G, QT, DENSE, THUMB><<<grid, kThreads, 0, stream>>>(p);
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {

@@ -12,6 +12,19 @@ constexpr int kMaxSplit = 64;    // max blocks per split (one workgroup)
 constexpr int kMaxPseudoMax = 64; // max sink + local blocks with the sink/local pseudo-max
 constexpr int kMaxRows = 16;     // query rows (query tokens x heads of a kv group) per workgroup
 constexpr size_t kWsAlign = 256;
+constexpr int kMaxParts = 4;     // workgroups sharing one split's attend work
+
+// Workgroups per split. When (sequence, kv head, split) units are too few to
+// fill the chip, P workgroups share a split: each scans and selects the whole
+// split (same kept set) and attends every P-th kept block, leaving one
+// partial each. A function of (B, Hq, n_splits) alone, so the workspace size
+// and a separate combine call agree with the decode.
+inline int split_parts_for(int B, int Hq, int n_splits) {
+  const long units = (long)B * Hq * n_splits;
+  if (units <= 0) return 1;
+  const long P = 2048 / units;   // about one round of resident workgroups at G = 4
+  return P < 1 ? 1 : (P > kMaxParts ? kMaxParts : (int)P);
+}
 
 // Q query tokens per sequence (Q = 1: ordinary decode). Query-head rows are
 // indexed (b * Q + i) * Hq + h throughout: q, out, lse, mask and partials.
@@ -28,8 +41,8 @@ struct DecodeParams {
   const int32_t* seq_lens; // [B]
   const int32_t* block_table;  // [B, table_stride] page of each block, or null (contiguous cache)
   int table_stride, num_pages; // paged cache: K/V [num_pages, Hkv, 64, D], kq/kscale alike
-  float* o_part;           // f32  [B, Q, Hq, n_splits, D]   (normalised per split)
-  float* lse_part;         // f32  [B, Q, Hq, n_splits]      (natural log)
+  float* o_part;           // f32  [B, Q, Hq, n_splits * split_parts, D]   (normalised per part)
+  float* lse_part;         // f32  [B, Q, Hq, n_splits * split_parts]      (natural log)
   uint8_t* mask;           // u8   [B, Q, Hq, nb_max] or null
   void* out;               // bf16 / f32 [B, Q, Hq, D]
   float* lse;              // f32 [B, Q, Hq]
@@ -37,6 +50,7 @@ struct DecodeParams {
   int max_seq_len, B, Q, Hq, Hkv, cap;
   int nb_max;              // ceil(max_seq_len / kBlockSize)
   int n_splits;            // ceil(nb_max / split_blocks)
+  int split_parts;         // workgroups per split (split_parts_for); partials per row = n_splits * split_parts
   int split_blocks;
   int sink, local;
   int pm_sink_local;       // 1: pseudo-max over the sink/local blocks; 0: split max

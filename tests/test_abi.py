@@ -134,11 +134,25 @@ def _decode_multi(**kw):
                               args["stream"])
 
 
+def _ws_expected(B, rows, Hq, L, S, d):
+    ns = -(-(-(-L // 64)) // S)
+    parts = min(4, max(1, 2048 // (B * Hq * ns)))   # workgroups per split
+    n = B * rows * ns * parts
+    return -(-n * d * 4 // 256) * 256 + -(-n * 4 // 256) * 256
+
+
 def test_multi_workspace_bytes():
-    for B, Q, Hq in ((4, 4, 32), (1, 16, 8), (2, 1, 32)):
-        assert ffd.ffd_decode_multi_workspace_bytes(B, Q, Hq, 128, 131072, 64, 32) == \
-            ffd.ffd_decode_workspace_bytes(B, Q * Hq, 128, 131072, 64, 32)
+    for B, Q, Hq, L in ((4, 4, 32, 131072), (1, 16, 8, 131072), (2, 1, 32, 131072), (1, 4, 32, 32768)):
+        assert ffd.ffd_decode_multi_workspace_bytes(B, Q, Hq, 128, L, 64, 32) == _ws_expected(B, Q * Hq, Hq, L, 32, 128)
+    assert ffd.ffd_decode_multi_workspace_bytes(1, 1, 32, 128, 32768, 64, 32) == \
+        ffd.ffd_decode_workspace_bytes(1, 32, 128, 32768, 64, 32)
     assert ffd.ffd_decode_multi_workspace_bytes(4, 0, 32, 128, 131072, 64, 32) == 0
+
+
+def test_small_grids_get_more_partials():
+    # 32K tokens, one sequence: 16 splits x 32 heads -> 4 workgroups per split
+    assert ffd.ffd_decode_workspace_bytes(1, 32, 128, 32768, 64, 32) == _ws_expected(1, 32, 32, 32768, 32, 128)
+    assert _ws_expected(1, 32, 32, 32768, 32, 128) > 4 * 32 * 16 * 128 * 3
 
 
 @pytest.mark.parametrize("kw,status,needle", [
