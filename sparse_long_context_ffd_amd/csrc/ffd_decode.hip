@@ -518,12 +518,12 @@ __device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<
 // 2*D bytes; pairs of chunks are XOR-swizzled by row so that the 16 rows x
 // 32 bytes one transposing read touches fall on distinct banks.
 template <int D>
+__device__ __forceinline__ int vt_swz(int r) {
+  return D == 128 ? (r & 7) << 1 : ((r >> 1) & 3) << 1;
+}
+template <int D>
 __device__ __forceinline__ int vt_off(int r, int q) {
-  if constexpr (D == 128) {
-    return r * 256 + ((q ^ ((r & 7) << 1)) << 4);
-  } else {
-    return r * 128 + ((q ^ (((r >> 1) & 3) << 1)) << 4);
-  }
+  return r * (2 * D) + ((q ^ vt_swz<D>(r)) << 4);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -595,6 +595,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   const int rbase = rr * ROWB + ((h & 3) >> 1) * 16 + (h & 1) * 8;
   const float zscale = p.sm_scale * kLog2e;
   const int nkept = sm.nkept;
+  const float qs = (THUMB && hv) ? sm.qsumf[h] : 0.f;
 
   for (int e = first; e < nkept; e += stride) {
     const int jb = j0 + sm.kidx[e];
@@ -641,7 +642,10 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     }
     // The thumbnail QK holds more registers (two accumulators, operand
     // conversion), so only a quarter of V is in flight across it: the whole
-    // tile would cost the second wave per SIMD.
+    // tile would cost the second wave per SIMD. (Loading V straight into LDS
+    // with global_load_lds_dwordx4 frees those registers, but the compiler
+    // then waits for every outstanding load, the V DMA included, before the
+    // first use of the codes, which serialises V behind QK: slower.)
     constexpr int VH = THUMB ? VL / 4 : VL;
     u32x4_t vr[VL];
 #pragma unroll
@@ -683,7 +687,6 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
           au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_u, qop[s], au, 0, 0, 0);
           ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_r, qop[s], ar, 0, 0, 0);
         }
-        const float qs = hv ? sm.qsumf[h] : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int src = 16 * T + 4 * g + r;   // the lane holding this row's scales
@@ -797,7 +800,10 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, flo
 // One workgroup per (split, kv head j, sequence b) serving R = G x QT query
 // rows: the G heads of the group for each of the (up to QT) query tokens.
 template <int D, int G, int QT, bool DENSE, bool THUMB>
-__global__ __launch_bounds__(kThreads) void fused_decode_kernel(const DecodeParams p) {
+// Two waves per SIMD: the LDS of two workgroups per CU allows no more, and
+// the registers must not allow fewer.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fused_decode_kernel(
+    const DecodeParams p) {
   constexpr int R = G * QT;
   static_assert(QT == 1 || !THUMB, "several query tokens only with the int4 sketch");
   __shared__ DecodeSmem<D, R> sm;
