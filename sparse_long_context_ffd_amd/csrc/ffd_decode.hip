@@ -9,30 +9,35 @@
 //
 // One workgroup = 4 wave64s owns `split_blocks` consecutive 64-token blocks of
 // one (sequence b, kv head j) and serves all G = Hq/Hkv query heads of the
-// group, so every K/V byte it reads is shared by the G heads.
+// group -- for Q query tokens per sequence, G x Q query rows -- so every K/V
+// byte it reads is shared by all of them. When the grid is too small to fill
+// the chip, P workgroups share a split (each scans and selects all of it and
+// attends every P-th kept block).
 //
-//  prologue  q[b, jG..jG+G) -> LDS: fp32 copy and int8 copy + per-head scale
+//  prologue  the query rows -> LDS: fp32 copy and int8 copy + per-row scale
 //            (the scan query).
 //  scan      each wave takes whole blocks; a quad of lanes owns one token (each
 //            lane 16 B of int4 codes for D=128), 16 tokens per wave load =
 //            1 KiB contiguous. Nibbles are moved to offset binary (x ^ 8 =
 //            code + 8, 0..15) so v_dot4_i32_i8 can take them; the 8*sum(q)
 //            excess is subtracted after the quad reduction. Block score =
-//            max over valid tokens -> LDS.
-//  select    wave 0: per head split max m~, threshold fl32(m~ - δ), forced
-//            sink/local blocks, mask store, and a ballot-compacted list of the
-//            blocks kept by at least one head of the group (with a per-head
-//            bit mask).
+//            max over valid tokens -> LDS. (Several query tokens: the scores
+//            of all rows are an int8 MFMA per tile; 2-bit thumbnails: dot4
+//            over codes spread to bytes.)
+//  select    wave 0: per row split max m~ (or the sink/local estimate),
+//            threshold fl32(m~ - δ), forced sink/local blocks, mask store, and
+//            a ballot-compacted list of the blocks kept by at least one row
+//            (with a per-row bit mask).
 //  attend    waves take kept blocks round-robin, one 64-token block at a
-//            time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the G query
-//            heads padded to 16 columns):
+//            time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the query
+//            rows padded to 16 columns):
 //              QK  A = K rows straight from HBM into registers (16 tokens x
 //                  32 dims per MFMA; each lane reads D/2 contiguous bytes of a
 //                  row), B = the bf16 query, 4*(D/32) MFMAs per block;
-//              softmax in the MFMA output layout (lane = head, 4 tokens per
-//                  tile); the running max of every head starts at the scan's
+//              softmax in the MFMA output layout (lane = row, 4 tokens per
+//                  tile); the running max of every row starts at the scan's
 //                  split max (the scan result reused to seed the softmax) so
-//                  rescaling is rare; heads skip blocks they did not keep;
+//                  rescaling is rare; rows skip blocks they did not keep;
 //              PV  A = P as bf16 hi + lo parts (~fp32 precision), B = V, staged
 //                  through a per-wave XOR-swizzled LDS tile and read with the
 //                  transposing ds_read_b64_tr_b16, 2*2*(D/16) MFMAs per block.
