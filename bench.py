@@ -38,10 +38,17 @@ DECODE_SOURCES = ["ffd_decode.hip", "ffd_device.h", "ffd_internal.h"]
 
 
 def kernel_source_hash() -> str:
+    """Hash of the decode kernel sources with comments and whitespace removed,
+    so that a counter summary stays valid across comment-only edits."""
+    import re
+
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
-        with open(os.path.join(ROOT, "sparse_long_context_ffd_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sparse_long_context_ffd_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
