@@ -533,6 +533,23 @@ __device__ __forceinline__ int vt_off(int r, int q) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// 2^x for x <= 0 with the hardware exp (v_exp_f32). exp2f adds a rescaling
+// path so that results below 2^-126 come out denormal; a softmax weight that
+// small relative to the running max contributes nothing, so it is not needed.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bf16 bit patterns of the thumbnail codes u = 0..3 (0, 1, 2, 3), as byte
+// tables for v_perm_b32: selector u picks the low byte, 4 + u the high byte.
+constexpr uint32_t kCodeBf16Lo = 0x40008000u;   // low bytes of 0x0000, 0x3F80, 0x4000, 0x4040
+constexpr uint32_t kCodeBf16Hi = 0x40403F00u;   // high bytes
+// Two bf16 values from the code bytes b0, b1 (each 0..3) of y: (u(b0), u(b1)).
+// sel01 / sel23 pick bytes 0,1 / 2,3 of y.
+template <uint32_t SEL>
+__device__ __forceinline__ uint32_t code_pair_bf16(uint32_t y) {
+  const uint32_t sel = __builtin_amdgcn_perm(y | 0x04040404u, y, SEL);   // (b, b + 4, b', b' + 4)
+  return __builtin_amdgcn_perm(kCodeBf16Hi, kCodeBf16Lo, sel);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): within each aligned group of 16
 // lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
 // i/4, 4+i/4, 8+i/4 and 12+i/4 of its group.
@@ -576,7 +593,21 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4_t u = u32x4_t{0u, 0u, 0u, 0u};
-      if (hv) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
+      if constexpr (!THUMB) {
+        if (hv) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
+      } else {
+        // thumbnail order (see the QK below): slot 4*kk + m of k-step s is
+        // dim 16*(s/2) + 4m + k0 + kk, k0 = 2*(s%2); dword m of that row part
+        // holds dims (4m + k0, 4m + k0 + 1)
+        if (hv) {
+          uint32_t dw[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            dw[m] = *reinterpret_cast<const uint32_t*>(qh + 16 * (s >> 1) + 4 * m + 2 * (s & 1));
+          u = u32x4_t{(dw[0] & 0xffffu) | (dw[1] << 16), (dw[2] & 0xffffu) | (dw[3] << 16),
+                      (dw[0] >> 16) | (dw[1] & 0xffff0000u), (dw[2] >> 16) | (dw[3] & 0xffff0000u)};
+        }
+      }
       qop[s] = as_bf16x8(u);
     }
   }
@@ -679,17 +710,29 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       for (int T = 0; T < 4; ++T) {
         f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f};
         f32x4_t ar = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // k-step s covers the lane's dims 16*(s/2) + 4m + k0 + kk (m = 0..3,
+        // kk = 0..1, k0 = 2*(s%2)) in slot 4*kk + m: byte m of
+        // (codes >> 2(k0 + kk)) & 0x03030303 is exactly the code of that dim,
+        // so each pair of bf16 codes is two byte permutes from a table; the
+        // residual byte of dim d is byte d%4 of word d/4, read by the convert.
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const uint32_t cbits = kc[T][s >> 1] >> (16 * (s & 1));
-          bf16x8_t a_u, a_r;
+          const int k0 = 2 * (s & 1);
+          const uint32_t w = kc[T][s >> 1];
+          const uint32_t y0 = (w >> (2 * k0)) & 0x03030303u;
+          const uint32_t y1 = (w >> (2 * k0 + 2)) & 0x03030303u;
+          const u32x4_t ub = u32x4_t{code_pair_bf16<0x05010400u>(y0), code_pair_bf16<0x07030602u>(y0),
+                                     code_pair_bf16<0x05010400u>(y1), code_pair_bf16<0x07030602u>(y1)};
+          bf16x8_t a_r;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            a_u[e] = (__bf16)(float)((cbits >> (2 * e)) & 3u);
-            const uint32_t word = (e < 4) ? kres[T][s].x : kres[T][s].y;
-            a_r[e] = (__bf16)(float)(int8_t)(word >> (8 * (e & 3)));
-          }
-          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_u, qop[s], au, 0, 0, 0);
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const u32x2_t rw = kres[T][2 * (s >> 1) + (m >> 1)];
+              const uint32_t word = (m & 1) ? rw.y : rw.x;
+              a_r[4 * kk + m] = (__bf16)(float)(int8_t)(word >> (8 * (k0 + kk)));
+            }
+          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ub), qop[s], au, 0, 0, 0);
           ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_r, qop[s], ar, 0, 0, 0);
         }
 #pragma unroll
@@ -735,7 +778,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     const bool up = mx > st.m;
     if (__ballot(up)) {
       const float mn = up ? mx : st.m;
-      const float alpha = (st.m == -INFINITY) ? 0.f : exp2f(st.m - mn);
+      const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - mn);
       st.m = mn;
       st.l *= alpha;
 #pragma unroll
@@ -750,7 +793,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
     for (int T = 0; T < 4; ++T)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = (sv[T][r] == -INFINITY) ? 0.f : exp2f(sv[T][r] - st.m);
+        const float pr = (sv[T][r] == -INFINITY) ? 0.f : fast_exp2(sv[T][r] - st.m);
         st.l += pr;
         const __bf16 hi = (__bf16)pr;
         const __bf16 lo = (__bf16)(pr - (float)hi);
