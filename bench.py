@@ -173,6 +173,8 @@ def main() -> int:
                     help="query tokens per sequence (ffd_decode_multi; token i sees the cache up to L - Q + i)")
     ap.add_argument("--paged", action="store_true",
                     help="keep the cache in a shuffled page pool and call ffd_decode_paged's kernels")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replays of the step captured in a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the delta=inf comparison")
@@ -325,6 +327,11 @@ def main() -> int:
             ev[2].record()
 
     def timed(dl, steps, warmup):
+        """Eager steps with HIP events around each launch (per-kernel times),
+        then -- unless --no-graph -- the same step captured once in a HIP graph
+        and replayed (the step's wall time without host launch gaps, as a
+        serving loop would issue it). Returns (wall per step in s, eager wall
+        per step in s, fused us[], combine us[])."""
         for _ in range(warmup):
             step(dl)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -333,13 +340,27 @@ def main() -> int:
         for i in range(steps):
             step(dl, evs[i])
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t_a
+        wall_eager = (time.perf_counter() - t_a) / steps
         fused = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
         comb = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
-        return wall, fused, comb
+        if args.no_graph:
+            return wall_eager, wall_eager, fused, comb
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(dl)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t_a = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_a) / steps
+        del g
+        return wall, wall_eager, fused, comb
 
-    wall, fused_us, comb_us = timed(delta, args.steps, args.warmup)
-    step_us_wall = wall / args.steps * 1e6
+    wall, wall_eager, fused_us, comb_us = timed(delta, args.steps, args.warmup)
+    step_us_wall = wall * 1e6
     m = mask.cpu().numpy()
     if Q > 1:
         m_rows = m
@@ -400,6 +421,8 @@ def main() -> int:
             "fused_p90": round(float(np.percentile(fused_us, 90)), 2),
             "combine_median": round(float(np.median(comb_us)), 2),
             "step_wall": round(step_us_wall, 2),
+            "step_wall_eager": round(wall_eager * 1e6, 2),
+            "step_timing": "eager launches" if args.no_graph else "replays of the step captured in a HIP graph",
             "quantize_build": round(quant_build_us, 1),
         },
         "bytes": {"scan": int(scan_b), "kv": int(kv_b)},
@@ -409,13 +432,13 @@ def main() -> int:
     }
 
     if not args.no_dense and not dense:
-        wall_d, fused_d, _ = timed(math.inf, max(10, args.steps // 5), 3)
+        wall_d, _, fused_d, _ = timed(math.inf, max(10, args.steps // 5), 3)
         md = mask.cpu().numpy()
         if Q > 1:
             md = md.max(axis=1)
         _, kv_d, _ = algorithmic_bytes(md, inp["seq_lens"], Hkv, G, d, w.block_size, True, args.storage)
         rec["dense_delta_inf"] = {
-            "us_per_step": round(wall_d / max(10, args.steps // 5) * 1e6, 2),
+            "us_per_step": round(wall_d * 1e6, 2),
             "fused_median_us": round(float(np.median(fused_d)), 2),
             "fused_GBps": round(kv_d / (float(fused_d.mean()) * 1e-6) / 1e9, 1),
             "sparse_speedup": round(float(np.median(fused_d)) / float(np.median(fused_us)), 3),
