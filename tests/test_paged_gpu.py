@@ -112,3 +112,52 @@ def test_paged_dense_path():
                                quantize=False)
     assert_close(out.cpu().numpy(), r_out, "paged dense out")
     assert_close(lse.cpu().numpy(), r_lse, "paged dense lse")
+
+
+@pytest.mark.parametrize("pm", ["split", "sink_local"])
+def test_paged_full_size_bit_identical(pm):
+    """The 128K x4 workload in the benchmark's paged configuration (shuffled
+    64-token pages): mask, output and LSE bit-identical to the contiguous call,
+    whose parity with the oracle at this size is tested elsewhere."""
+    from ffd_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS["llama3_8b_128k_b4"]
+    say(f"paged full size {w.name} ({pm}): generating")
+    inp = make_inputs(w)
+    dv = to_device(inp)
+    B, Hkv, cap, d = dv["k"].shape
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    nbs = [-(-int(L) // 64) for L in inp["seq_lens"]]
+    num_pages = sum(nbs)
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(11)).to(torch.int32)
+    stride = cap // 64
+    table = torch.zeros((B, stride), dtype=torch.int32)
+    pools = [torch.empty((num_pages, Hkv, 64) + tuple(x.shape[3:]), dtype=x.dtype, device="cuda")
+             for x in (dv["k"], dv["v"], kq, ks)]
+    used = 0
+    for b in range(B):
+        table[b, :nbs[b]] = perm[used:used + nbs[b]]
+        pages = table[b, :nbs[b]].to("cuda", torch.int64)
+        used += nbs[b]
+        for x, pool in zip((dv["k"], dv["v"], kq, ks), pools):
+            pool[pages] = x[b, :, :64 * nbs[b]].reshape((Hkv, nbs[b], 64) + tuple(x.shape[3:])).transpose(0, 1)
+    table = table.cuda()
+    kw = dict(max_seq_len=cap, block_size=64, delta=w.deltas[0], sink=w.sink, local=w.local,
+              split_blocks=w.split_blocks, sm_scale=sm_scale_for(d), pseudo_max=pm)
+    res = []
+    for paged in (False, True):
+        out = torch.empty((B, w.Hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, w.Hq), dtype=torch.float32, device="cuda")
+        mask = torch.empty((B, w.Hq, cap // 64), dtype=torch.uint8, device="cuda")
+        ws = ffd.alloc_workspace(B, w.Hq, d, cap, 64, w.split_blocks)
+        say(f"  {'paged' if paged else 'contiguous'} decode")
+        if paged:
+            ffd.ffd_decode_paged(dv["q"], pools[0], pools[1], pools[2], pools[3], table, dv["seq_lens"], out=out,
+                                 lse=lse, kept_mask=mask, workspace=ws, **kw)
+        else:
+            ffd.ffd_decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], out=out, lse=lse, kept_mask=mask,
+                           workspace=ws, **kw)
+        torch.cuda.synchronize()
+        res.append((out, lse, mask))
+    for a, b_ in zip(res[0], res[1]):
+        assert torch.equal(a, b_)
