@@ -184,8 +184,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the decode path has no multi-GPU mode here.", file=sys.stderr)
+        print(f"bench.py: the decode path runs on one GPU (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "it has no multi-GPU mode: sequences would be sharded by whole splits, with only the per-split "
+              "partials exchanged before ffd_combine.", file=sys.stderr)
         return 2
 
     import numpy as np
