@@ -1031,15 +1031,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // ---------------------------------------------------------------------------
 // split combine: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s
 // ---------------------------------------------------------------------------
-// One workgroup per (sequence, query head): wave 0 forms the merged LSE; then
-// PARTS groups of D threads each sum an interleaved quarter of the splits
-// (four loads in flight per thread) and the parts are added in a fixed order.
+// One workgroup per (query-head row, 32 output dims): wave 0 forms the merged
+// LSE over the row's partials; 8 groups of 32 threads each sum an interleaved
+// eighth of the partials (four loads in flight per thread) and the groups are
+// added in a fixed order (deterministic). Spreading a row over D/32
+// workgroups keeps the short latency chain of a long sequence's many
+// partials off one workgroup.
+constexpr int kCombineDims = 32;
+constexpr int kCombineThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
-  constexpr int PARTS = 512 / D;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const DecodeParams p) {
+  constexpr int PARTS = kCombineThreads / kCombineDims;
   __shared__ float s_lse;
-  __shared__ float red[PARTS][D];
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ float red[PARTS][kCombineDims];
+  const int h = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * kCombineDims, tid = threadIdx.x;
   int L = p.seq_lens[b];
   L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
   const int NB = (L + kBlockSize - 1) / kBlockSize;
@@ -1047,14 +1053,14 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
   const size_t bh = (size_t)b * p.Q * p.Hq + h;   // row (b, query token h / Hq, head h % Hq)
   const size_t per_row = (size_t)p.n_splits * p.split_parts;
   const float* lp = p.lse_part + bh * per_row;
-  const float* op = p.o_part + bh * per_row * D;
+  const float* op = p.o_part + bh * per_row * D + c0;
   if (tid < kWave) {
     const float l = merged_lse(lp, ns, tid);
     if (tid == 0) s_lse = l;
   }
   __syncthreads();
   const float lse = s_lse;
-  const int c = tid % D, part = tid / D;
+  const int c = tid % kCombineDims, part = tid / kCombineDims;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (lse != -INFINITY) {
     int s = part;
@@ -1070,8 +1076,8 @@ __global__ __launch_bounds__(512) void combine_kernel(const DecodeParams p) {
     float res = 0.f;
 #pragma unroll
     for (int q = 0; q < PARTS; ++q) res += red[q][c];
-    store_out(p, bh * D + c, res);
-    if (c == 0) p.lse[bh] = lse;
+    store_out(p, bh * D + c0 + c, res);
+    if (c0 == 0 && c == 0) p.lse[bh] = lse;
   }
 }
 
@@ -1083,7 +1089,7 @@ hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) 
     fused_decode_kernel<D, G, QT, DENSE, THUMB><<<grid, kThreads, 0, stream>>>(p);
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
-    combine_kernel<D><<<dim3(p.Q * p.Hq, p.B), 512, 0, stream>>>(p);
+    combine_kernel<D><<<dim3(p.Q * p.Hq, p.B, D / kCombineDims), kCombineThreads, 0, stream>>>(p);
   }
   return hipGetLastError();
 }
