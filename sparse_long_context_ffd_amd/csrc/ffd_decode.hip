@@ -16,14 +16,13 @@
 //
 //  prologue  the query rows -> LDS: fp32 copy and int8 copy + per-row scale
 //            (the scan query).
-//  scan      each wave takes whole blocks; a quad of lanes owns one token (each
-//            lane 16 B of int4 codes for D=128), 16 tokens per wave load =
-//            1 KiB contiguous. Nibbles are moved to offset binary (x ^ 8 =
-//            code + 8, 0..15) so v_dot4_i32_i8 can take them; the 8*sum(q)
-//            excess is subtracted after the quad reduction. Block score =
-//            max over valid tokens -> LDS. (Several query tokens: the scores
-//            of all rows are an int8 MFMA per tile; 2-bit thumbnails: dot4
-//            over codes spread to bytes.)
+//  scan      each wave takes whole blocks, 16-token tiles; lane (g, n) holds
+//            D/8 bytes of int4 codes of token n (16 tokens x D/2 B = one
+//            contiguous wave load). Nibbles are moved to offset binary (x ^ 8
+//            = code + 8, 0..15) and all query rows' dots are one
+//            v_mfma_i32_16x16x64_i8 per 64 dims; the 8*sum(q) excess is
+//            subtracted after. Block score = max over valid tokens -> LDS.
+//            (2-bit thumbnails: the codes spread to bytes, same MFMA.)
 //  select    wave 0: per row split max m~ (or the sink/local estimate),
 //            threshold fl32(m~ - δ), forced sink/local blocks, mask store, and
 //            a ballot-compacted list of the blocks kept by at least one row
@@ -129,245 +128,24 @@ __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) 
 }
 
 // ---------------------------------------------------------------------------
-// scan: tentative block scores for the G heads ([TS] Methodology 3, "Top-δ
-// Selection": stream the low-bit keys, compute tentative scores per block)
+// scan: tentative block scores ([TS] Methodology 3, "Top-δ Selection": stream
+// the low-bit keys, compute tentative scores per block)
 // ---------------------------------------------------------------------------
-template <int D, int G>
-// Scores of the split's nblk_split blocks (block j0 + i -> sm.blk[i]) followed
-// by nx extra blocks (sm.xidx[x] -> sm.xblk[x]), in one pass.
-__device__ __forceinline__ void scan_blocks(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j, int j0,
-                                            int nblk_split, int nx, int L, int lane, int w) {
-  const int nblk = nblk_split + nx;
-  constexpr int NCW = D / 32;  // 32-bit code words per lane (8 codes each)
-  const int quad = lane >> 2;
-  const int ql = lane & 3;
-  // this lane's slice of the int8 query: elements [ql*D/4, ql*D/4 + D/4)
-  int qe[G][NCW], qo[G][NCW];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int i = 0; i < NCW; ++i) {
-      const int8_t* s = &sm.qc[h][ql * (D / 4) + 8 * i];
-      qe[h][i] = pack4_i8(s[0], s[2], s[4], s[6]);
-      qo[h][i] = pack4_i8(s[1], s[3], s[5], s[7]);
-    }
-  }
-  int corr[G];
-  float cq[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    corr[h] = 8 * sm.sumq[h];
-    cq[h] = sm.cq[h];
-  }
-
-  // Each wave owns blocks w, w+4, w+8, ...; kChunk of them are loaded at once
-  // (kChunk*4 KiB of codes in flight per wave) before any is reduced.
-  constexpr int kChunk = 4;
-  for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
-    u32x4_t cw[kChunk][4];
-    float sc[kChunk][4];
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int jl = jc + c * kWaves;
-      if (jl < nblk) {
-        const int jb = jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split];
-        const int t0 = jb * kBlockSize;
-        const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
-        const uint8_t* kq = p.kq + r0 * (D / 2);
-        const float* ks = p.kscale + r0;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int t = t0 + it * 16 + quad;
-          const bool ok = t < L;
-          const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * (D / 2) + ql * (D / 8);
-          if constexpr (NCW == 4) {
-            cw[c][it] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
-          } else {
-            const uint2 u = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
-            cw[c][it] = u32x4_t{u.x, u.y, 0u, 0u};
-          }
-          sc[c][it] = ok ? __builtin_nontemporal_load(ks + (t - t0)) : 0.f;
-        }
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int jl = jc + c * kWaves;
-      if (jl >= nblk) continue;
-      const int t0 = (jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split]) * kBlockSize;
-      float bm[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        int acc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = 0;
-#pragma unroll
-        for (int i = 0; i < NCW; ++i) {
-          const uint32_t x = cw[c][it][i] ^ 0x88888888u;   // two's complement -> code + 8
-          const int lo = (int)(x & 0x0f0f0f0fu);
-          const int hi = (int)((x >> 4) & 0x0f0f0f0fu);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h] = __builtin_amdgcn_sdot4(lo, qe[h][i], acc[h], false);
-            acc[h] = __builtin_amdgcn_sdot4(hi, qo[h][i], acc[h], false);
-          }
-        }
-        const bool ok = t0 + it * 16 + quad < L;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const int dot = quad_sum_i(acc[h]) - corr[h];
-          const float wgt = sc[c][it] * cq[h];
-          const float sv = (float)dot * wgt;
-          if (ok) bm[h] = fmaxf(bm[h], sv);
-        }
-      }
-      // max over the 16 quads (each quad's lanes hold identical values)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float m = bm[h];
-        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
-        m = fmaxf(m, dpp_f<kDppMirror>(m));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        bm[h] = m;
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          if (jl < nblk_split) sm.blk[jl][h] = bm[h];
-          else sm.xblk[jl - nblk_split][h] = bm[h];
-        }
-      }
-    }
-  }
-}
-
-// Thumbnail scan: the same block scores from 2-bit codes u ([TS] Methodology
-// 1: the thumbnails are what the scan streams). dot = 2 * sum qc*u - 3 * sum qc
-// (exact integer); s^ = fl32(float(dot) * fl32(t * cq)). A quad of lanes owns a
-// token; each lane D/64 code words (16 codes each); byte m of
-// (word >> 2k) & 0x03030303 is code 4m + k, matched by a permuted query.
-template <int D, int G>
-__device__ __forceinline__ void scan_blocks_thumb(const DecodeParams& p, DecodeSmem<D, G>& sm, int b, int j,
-                                                  int j0, int nblk_split, int nx, int L, int lane, int w) {
-  constexpr int NW = D / 64;   // code words per lane
-  const int nblk = nblk_split + nx;
-  const int quad = lane >> 2;
-  const int ql = lane & 3;
-  int qp[G][NW][4];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < NW; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int8_t* s = &sm.qc[h][ql * (D / 4) + 16 * i + k];
-        qp[h][i][k] = pack4_i8(s[0], s[4], s[8], s[12]);
-      }
-  int corr[G];
-  float cq[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    corr[h] = 3 * sm.sumq[h];
-    cq[h] = sm.cq[h];
-  }
-  // Codes are half the bytes of the int4 sketch, so twice as many blocks are
-  // kept in flight per wave to keep the same bytes outstanding.
-  constexpr int kChunk = 8;
-  for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
-    uint32_t cw[kChunk][4][NW];
-    float sc[kChunk];   // scale of token 16*ql + quad of each block
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int jl = jc + c * kWaves;
-      if (jl < nblk) {
-        const int jb = jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split];
-        const int t0 = jb * kBlockSize;
-        const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
-        const uint8_t* k2 = p.k2 + r0 * (D / 4);
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int t = t0 + it * 16 + quad;
-          const bool ok = t < L;
-          const uint8_t* src = k2 + (size_t)(ok ? t - t0 : 0) * (D / 4) + ql * (D / 16);
-          if constexpr (NW == 2) {
-            const u32x2_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{0u, 0u};
-            cw[c][it][0] = u.x;
-            cw[c][it][1] = u.y;
-          } else {
-            cw[c][it][0] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src)) : 0u;
-          }
-        }
-        const int ts = 16 * ql + quad;
-        sc[c] = (t0 + ts < L) ? __builtin_nontemporal_load(p.k2scale + r0 + ts) : 0.f;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const int jl = jc + c * kWaves;
-      if (jl >= nblk) continue;
-      const int t0 = (jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split]) * kBlockSize;
-      float bm[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) bm[h] = -INFINITY;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        int acc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h] = 0;
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int bytes = (int)((cw[c][it][i] >> (2 * k)) & 0x03030303u);
-#pragma unroll
-            for (int h = 0; h < G; ++h) acc[h] = __builtin_amdgcn_sdot4(bytes, qp[h][i][k], acc[h], false);
-          }
-        // every lane of the quad holds token it*16 + quad's dot; the lane with
-        // ql == it also holds its scale
-        const bool ok = (ql == it) && (t0 + it * 16 + quad < L);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const int dot = 2 * quad_sum_i(acc[h]) - corr[h];
-          const float wgt = sc[c] * cq[h];
-          const float sv = (float)dot * wgt;
-          if (ok) bm[h] = fmaxf(bm[h], sv);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float m = bm[h];
-        m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-        m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
-        m = fmaxf(m, dpp_f<kDppMirror>(m));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        bm[h] = m;
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          if (jl < nblk_split) sm.blk[jl][h] = bm[h];
-          else sm.xblk[jl - nblk_split][h] = bm[h];
-        }
-      }
-    }
-  }
-}
-
-// Multi-query scan (Q > 1 query tokens, int4 sketch): the R = G x Q rows'
-// scores are one small integer matrix product per 16-token tile, done on the
+// int4 scan: the R query rows' scores (the G heads, or G x Q for Q query
+// tokens) are one small integer matrix product per 16-token tile, done on the
 // matrix cores (v_mfma_i32_16x16x64_i8; exact int32): A = the int8 queries
 // (row n = lane % 16), B = the tile's codes moved to offset binary (code + 8,
 // token column n = lane % 16); lane group g = lane / 16 holds dims
 // g*D/4 .. +D/4 of both, in the order the nibbles are unpacked. Output lane
 // (g, n) holds rows 4g..4g+3 of token n; the 8*sum(q) excess is subtracted and
-// s^ = fl32(float(dot) * fl32(scale * cq)) as in the single-query scan. Each
-// row only counts the tokens its query token sees.
-template <int D, int G, int QT>
+// s^ = fl32(float(dot) * fl32(scale * cq)). Each row only counts the tokens
+// its query token sees. (A v_dot4_i32_i8 scan, a quad of lanes per token,
+// measured slower: 371 vs 365 us at 128K x4, 45 vs 41 us at 32K.)
+// THUMB: the 2-bit thumbnail codes u instead ([TS] Methodology 1: the
+// thumbnails are what the scan streams): operand word e of MFMA s is
+// (codes >> 2e) & 0x03030303, whose byte m is the code of dim 16s + 4m + e;
+// dot = 2 * sum qc*u - 3 * sum qc, s^ = fl32(float(dot) * fl32(t * cq)).
+template <int D, int G, int QT, bool THUMB>
 __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
                                                int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
   constexpr int R = G * QT;
@@ -375,21 +153,28 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
   const int nblk = nblk_split + nx;
   const int n = lane & 15;
   const int g = lane >> 4;
-  // A operand: word e of MFMA s holds dims g*D/4 + 8*(2s + e/2) + 2*i + (e & 1), i = 0..3
+  // A operand: word e of MFMA s holds dims g*D/4 + 8*(2s + e/2) + 2*i + (e & 1)
+  // (int4) or g*D/4 + 16s + 4i + e (thumbnail), i = 0..3
   i32x4_t qa[NM];
 #pragma unroll
   for (int s = 0; s < NM; ++s)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int8_t* q8 = &sm.qc[n < R ? n : 0][g * (D / 4) + 8 * (2 * s + e / 2) + (e & 1)];
-      qa[s][e] = n < R ? pack4_i8(q8[0], q8[2], q8[4], q8[6]) : 0;
+      const int8_t* qrow = &sm.qc[n < R ? n : 0][g * (D / 4)];
+      if constexpr (THUMB) {
+        const int8_t* q8 = qrow + 16 * s + e;
+        qa[s][e] = n < R ? pack4_i8(q8[0], q8[4], q8[8], q8[12]) : 0;
+      } else {
+        const int8_t* q8 = qrow + 8 * (2 * s + e / 2) + (e & 1);
+        qa[s][e] = n < R ? pack4_i8(q8[0], q8[2], q8[4], q8[6]) : 0;
+      }
     }
   int corr[4], Lr[4];
   float cq[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rr = 4 * g + r;
-    corr[r] = rr < R ? 8 * sm.sumq[rr] : 0;
+    corr[r] = rr < R ? (THUMB ? 3 : 8) * sm.sumq[rr] : 0;
     cq[r] = rr < R ? sm.cq[rr] : 0.f;
     Lr[r] = rr < R ? row_len<G>(p, sl, rr) : 0;
   }
@@ -405,19 +190,24 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
         const int jb = jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split];
         const int t0 = jb * kBlockSize;
         const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
-        const uint8_t* kq = p.kq + r0 * (D / 2);
+        constexpr int RB = THUMB ? D / 4 : D / 2;   // code bytes per token
+        const uint8_t* kq = (THUMB ? p.k2 : p.kq) + r0 * RB;
+        const float* ks = (THUMB ? p.k2scale : p.kscale) + r0;
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
           const int t = t0 + 16 * T + n;
           const bool ok = t < L;
-          const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * (D / 2) + g * (D / 8);
-          if constexpr (D == 128) {
+          const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * RB + g * (RB / 4);
+          if constexpr (RB / 4 == 16) {
             cw[c][T] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
-          } else {
+          } else if constexpr (RB / 4 == 8) {
             const u32x2_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{0u, 0u};
             cw[c][T] = u32x4_t{u.x, u.y, 0u, 0u};
+          } else {
+            const uint32_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src)) : 0u;
+            cw[c][T] = u32x4_t{u, 0u, 0u, 0u};
           }
-          sc[c][T] = ok ? __builtin_nontemporal_load(p.kscale + r0 + (t - t0)) : 0.f;
+          sc[c][T] = ok ? __builtin_nontemporal_load(ks + (t - t0)) : 0.f;
         }
       }
     }
@@ -432,17 +222,25 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
         i32x4_t acc = i32x4_t{0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < NM; ++s) {
-          const uint32_t x0 = cw[c][T][2 * s] ^ 0x88888888u;   // two's complement -> code + 8
-          const uint32_t x1 = cw[c][T][2 * s + 1] ^ 0x88888888u;
-          const i32x4_t kb = i32x4_t{(int)(x0 & 0x0f0f0f0fu), (int)((x0 >> 4) & 0x0f0f0f0fu),
-                                     (int)(x1 & 0x0f0f0f0fu), (int)((x1 >> 4) & 0x0f0f0f0fu)};
+          i32x4_t kb;
+          if constexpr (THUMB) {
+            const uint32_t x = cw[c][T][s];
+            kb = i32x4_t{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
+                         (int)((x >> 6) & 0x03030303u)};
+          } else {
+            const uint32_t x0 = cw[c][T][2 * s] ^ 0x88888888u;   // two's complement -> code + 8
+            const uint32_t x1 = cw[c][T][2 * s + 1] ^ 0x88888888u;
+            kb = i32x4_t{(int)(x0 & 0x0f0f0f0fu), (int)((x0 >> 4) & 0x0f0f0f0fu), (int)(x1 & 0x0f0f0f0fu),
+                         (int)((x1 >> 4) & 0x0f0f0f0fu)};
+          }
           acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[s], kb, acc, 0, 0, 0);
         }
         const int t = t0 + 16 * T + n;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float wgt = sc[c][T] * cq[r];
-          const float sv = (float)(acc[r] - corr[r]) * wgt;
+          const int dot = THUMB ? 2 * acc[r] - corr[r] : acc[r] - corr[r];
+          const float sv = (float)dot * wgt;
           if (t < Lr[r]) bm[r] = fmaxf(bm[r], sv);
         }
       }
@@ -956,9 +754,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // sink/local pseudo-max: the sink and local blocks outside this split are
     // listed in the prologue and scanned in the same pass as the split
     const int nx = p.pm_sink_local ? sm.nx : 0;
-    if constexpr (QT > 1) scan_blocks_mq<D, G, QT>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
-    else if constexpr (THUMB) scan_blocks_thumb<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
-    else scan_blocks<D, G>(p, sm, b, j, j0, nblk, nx, L, lane, w);
+    scan_blocks_mq<D, G, QT, THUMB>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
     __syncthreads();
     if (p.pm_sink_local && tid < R) {
       const int NBr = (row_len<G>(p, sl, tid) + kBlockSize - 1) / kBlockSize;
