@@ -26,10 +26,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // quad_perm [1,0,3,2] and [2,3,0,1]; row_half_mirror (lane i <-> 7-i within
 // each 8-lane half row); row_mirror (lane i <-> 15-i within each 16-lane row).
 template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
-}
-template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
@@ -37,24 +33,6 @@ constexpr int kDppQuadXor1 = 0xb1;
 constexpr int kDppQuadXor2 = 0x4e;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
-
-// Sum over each aligned group of 4 lanes; every lane of the group gets it.
-__device__ __forceinline__ int quad_sum_i(int x) {
-  x += dpp_i<kDppQuadXor1>(x);
-  x += dpp_i<kDppQuadXor2>(x);
-  return x;
-}
-
-// Sum over aligned groups of N lanes (N in {8, 16}); every lane gets it.
-template <int N>
-__device__ __forceinline__ float group_sum_f(float x) {
-  static_assert(N == 8 || N == 16, "group size");
-  x += dpp_f<kDppQuadXor1>(x);
-  x += dpp_f<kDppQuadXor2>(x);
-  x += dpp_f<kDppHalfMirror>(x);
-  if constexpr (N == 16) x += dpp_f<kDppMirror>(x);
-  return x;
-}
 
 __device__ __forceinline__ float wave_max_f(float x) {
 #pragma unroll
