@@ -85,6 +85,8 @@ struct DecodeSmem {
   int nkept;
   float wm[kWaves][R];
   float wl[kWaves][R];
+  float wa[kWaves][R];      // epilogue: each wave's weight in the row's merge
+  float rlse[R];            // epilogue: the row's natural-log LSE
 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -803,24 +805,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __syncthreads();
 
   // ---- epilogue: merge waves, write the split partial -------------------
-  for (int i = tid; i < R * D; i += kThreads) {
-    const int h = i / D, cc = i % D;
-    if (h / G >= p.Q) continue;
+  // per row, once: the waves' weights exp2(m_w - m) / den and the LSE
+  if (tid < R) {
+    const int h = tid;
     float mx = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, sm.wm[ww][h]);
-    float den = 0.f, num = 0.f;
+    float a[kWaves], den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float a = (sm.wm[ww][h] == -INFINITY) ? 0.f : exp2f(sm.wm[ww][h] - mx);
-      den += sm.wl[ww][h] * a;
-      num += sm.wo[ww][h][cc] * a;
+      a[ww] = (sm.wm[ww][h] == -INFINITY) ? 0.f : exp2f(sm.wm[ww][h] - mx);
+      den += sm.wl[ww][h] * a[ww];
     }
-    const size_t row = (row_index<G>(p, b, j, h) * p.n_splits + split) * p.split_parts + part;
     // a row can keep no block of a split (sink/local pseudo-max, or a query
-    // token that does not see the split): empty partial
-    p.o_part[row * D + cc] = den > 0.f ? num / den : 0.f;
-    if (cc == 0) p.lse_part[row] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+    // token that does not see the split): empty partial, weight 0
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) sm.wa[ww][h] = den > 0.f ? a[ww] / den : 0.f;
+    sm.rlse[h] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  for (int i = tid; i < R * D; i += kThreads) {
+    const int h = i / D, cc = i % D;
+    if (h / G >= p.Q) continue;
+    float o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) o += sm.wo[ww][h][cc] * sm.wa[ww][h];
+    const size_t row = (row_index<G>(p, b, j, h) * p.n_splits + split) * p.split_parts + part;
+    p.o_part[row * D + cc] = o;
+    if (cc == 0) p.lse_part[row] = sm.rlse[h];
   }
 }
 
