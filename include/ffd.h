@@ -36,7 +36,7 @@ extern "C" {
 typedef enum {
   FFD_OK = 0,
   FFD_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad scalar, misaligned pointer */
-  FFD_ERR_UNSUPPORTED = 2, /* valid request that the kernels do not implement (d, block size, G, S) */
+  FFD_ERR_UNSUPPORTED = 2, /* valid request the kernels do not implement (d, block size, G, G*Q, S, sink+local) */
   FFD_ERR_WORKSPACE = 3,   /* workspace smaller than ffd_decode_workspace_bytes() */
   FFD_ERR_HIP = 4          /* a HIP launch error */
 } ffd_status;
