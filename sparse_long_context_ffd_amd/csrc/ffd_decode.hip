@@ -758,18 +758,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int nx = p.pm_sink_local ? sm.nx : 0;
     scan_blocks_mq<D, G, QT, THUMB>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
     __syncthreads();
-    if (p.pm_sink_local && tid < R) {
-      const int NBr = (row_len<G>(p, sl, tid) + kBlockSize - 1) / kBlockSize;
-      float m = -INFINITY;
-      for (int x = 0; x < nx; ++x) {
-        const int jb = sm.xidx[x];
-        if (jb < NBr && (jb < p.sink || jb >= NBr - p.local)) m = fmaxf(m, sm.xblk[x][tid]);
+    // m~ per row over its own sink and local blocks: wave 0, one lane per
+    // scored block (the extra ones first, then the split's), wave max per row
+    if (p.pm_sink_local && w == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int NBr = (row_len<G>(p, sl, r) + kBlockSize - 1) / kBlockSize;
+        float m = -INFINITY;
+        for (int i = lane; i < nx + nblk; i += kWave) {
+          const int jb = i < nx ? sm.xidx[i] : j0 + (i - nx);
+          const float sc = i < nx ? sm.xblk[i][r] : sm.blk[i - nx][r];
+          if (jb < NBr && (jb < p.sink || jb >= NBr - p.local)) m = fmaxf(m, sc);
+        }
+        m = wave_max_f(m);
+        if (lane == 0) sm.pm[r] = m;
       }
-      for (int jl = 0; jl < nblk; ++jl) {
-        const int jb = j0 + jl;
-        if (jb < NBr && (jb < p.sink || jb >= NBr - p.local)) m = fmaxf(m, sm.blk[jl][tid]);
-      }
-      sm.pm[tid] = m;
     }
     if (p.pm_sink_local) __syncthreads();
   }
