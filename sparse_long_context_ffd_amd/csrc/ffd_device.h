@@ -34,9 +34,15 @@ constexpr int kDppQuadXor2 = 0x4e;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// Max over the wave; every lane gets it. The steps inside each 16-lane row are
+// DPP moves (VALU latency), only the two steps across rows go through LDS.
 __device__ __forceinline__ float wave_max_f(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
   return x;
 }
 
