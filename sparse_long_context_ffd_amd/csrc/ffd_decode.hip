@@ -60,14 +60,15 @@ constexpr int kWaves = kThreads / kWave;
 // or G x Q for Q query tokens (row r = token r / G, head r % G).
 template <int D, int R>
 struct DecodeSmem {
-  // The V tiles are live only during attend: the prologue's fp32 query and
-  // the epilogue's per-wave partial outputs reuse their space.
-  union {
+  // The V tiles are live only during attend: the bf16 query rows (read into
+  // registers at its start) and the epilogue's per-wave partial outputs reuse
+  // their space.
+  union alignas(16) {
     uint16_t vt[kWaves][kBlockSize * D];  // per-wave V tile (bf16, swizzled rows)
-    float q[R][D];                        // bf16 query widened to fp32 (prologue)
+    uint16_t qb[R][D];                    // bf16 query rows
     float wo[kWaves][R][D];               // per-wave partial outputs (epilogue)
   };
-  int8_t qc[R][D];          // int8 scan query
+  alignas(16) int8_t qc[R][D];  // int8 scan query
   static_assert(sizeof(float) * R <= sizeof(uint16_t) * kBlockSize, "wave partials must fit the V tiles");
   static_assert(R <= kMaxRows, "at most 16 query rows per workgroup");
   float cq[R];              // fl32(sq * sm_scale)
@@ -82,6 +83,7 @@ struct DecodeSmem {
   int rowp[kMaxSplit];      // paged cache: first cache row of each block of the split
   uint8_t kidx[kMaxSplit];  // kept blocks (split-local index)
   uint16_t khm[kMaxSplit];  // per-row keep bits of each kept block
+  uint16_t hmb[kMaxSplit];  // per-row keep bits of every block of the split (mask)
   int nkept;
   float wm[kWaves][R];
   float wl[kWaves][R];
@@ -278,7 +280,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
 // is never kept for it, and its sink/local blocks are those of its own range.
 template <int D, int G, int QT, bool DENSE>
 __device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
-                                              int j0, int nblk, int nmask, int sl, int lane) {
+                                              int j0, int nblk, int sl, int lane) {
   constexpr int R = G * QT;
   const int jl = lane;
   const int jb = j0 + jl;
@@ -300,11 +302,7 @@ __device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<
       if (lane == 0) sm.seed[r] = mt;
     }
   }
-  if (p.mask != nullptr && jl < nmask) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r / G < p.Q) p.mask[row_index<G>(p, b, j, r) * p.nb_max + jb] = (uint8_t)((hm >> r) & 1u);
-  }
+  sm.hmb[jl] = (uint16_t)hm;   // the mask is written in the epilogue
   const unsigned long long bal = __ballot(hm != 0u);
   const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
   if (hm != 0u) {
@@ -389,7 +387,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   // B operand of QK: the bf16 query of row h, dims g*D/4 + 8s .. +8 for k-step s
   bf16x8_t qop[KS];
   {
-    const uint16_t* qh = p.q + row_index<G>(p, b, j, hv ? h : 0) * D + g * (D / 4);
+    const uint16_t* qh = &sm.qb[hv ? h : 0][g * (D / 4)];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4_t u = u32x4_t{0u, 0u, 0u, 0u};
@@ -432,6 +430,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   const float zscale = p.sm_scale * kLog2e;
   const int nkept = sm.nkept;
   const float qs = (THUMB && hv) ? sm.qsumf[h] : 0.f;
+  __syncthreads();   // the query rows share their space with the V tiles
 
   for (int e = first; e < nkept; e += stride) {
     const int jb = j0 + sm.kidx[e];
@@ -667,6 +666,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (split >= p.n_splits) return;
   }
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  // the query rows, one 16-byte chunk per thread, in flight from the start
+  constexpr int QC = D / 8;   // 16-byte chunks per query row
+  static_assert(R * QC <= kThreads, "one query chunk per thread");
+  const int qr = tid / QC, qk = tid % QC;
+  u32x4_t qw = u32x4_t{0u, 0u, 0u, 0u};
+  if (qr < R && qr / G < p.Q) qw = *reinterpret_cast<const u32x4_t*>(p.q + row_index<G>(p, b, j, qr) * D + qk * 8);
   const int sl = p.seq_lens[b];
   // the last query token sees the whole sequence: every load is bounded by it
   const int L = row_len<G>(p, sl, G * (p.Q - 1));
@@ -686,10 +691,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int nblk = min(p.split_blocks, NB - j0);
 
   // ---- prologue: query rows to LDS, int8 scan query -----------------------
-  for (int i = tid; i < R * D; i += kThreads) {
-    const int r = i / D;
-    sm.q[r][i % D] = (r / G < p.Q) ? bf16_to_f32(p.q[row_index<G>(p, b, j, r) * D + i % D]) : 0.f;
-  }
   if (p.block_table != nullptr && tid < nblk)
     sm.rowp[tid] = (int)(cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, j0 + tid) /
                          kBlockSize);
@@ -706,46 +707,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
     sm.nx = nx;
   }
-  __syncthreads();
-  for (int h = w; h < R; h += kWaves) {
-    constexpr int PER = D / kWave;
-    float x[PER];
+  if (qr < R) {
+    // row qr's chunks sit in QC consecutive lanes: its reductions stay there
+    *reinterpret_cast<u32x4_t*>(&sm.qb[qr][qk * 8]) = qw;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(qw[e]);
+      x[2 * e + 1] = bf16_hi(qw[e]);
+    }
     float amax = 0.f;
 #pragma unroll
-    for (int r = 0; r < PER; ++r) {
-      x[r] = sm.q[h][lane + r * kWave];
-      amax = fmaxf(amax, fabsf(x[r]));
-    }
-    amax = wave_max_f(amax);
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = group_max_f<QC>(amax);
     if constexpr (THUMB) {
       float fs = 0.f;
 #pragma unroll
-      for (int r = 0; r < PER; ++r) fs += x[r];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) fs += __shfl_xor(fs, o);
-      if (lane == 0) sm.qsumf[h] = fs;
+      for (int e = 0; e < 8; ++e) fs += x[e];
+      fs = group_sum_f<QC>(fs);
+      if (qk == 0) sm.qsumf[qr] = fs;
     }
-    int qsum = 0;
     if constexpr (!DENSE) {
       // amax < 2^-120 counts as a zero query: 127/amax would overflow to +inf
       const bool nz = amax >= 0x1p-120f;
+      int qsum = 0;
+      uint32_t cw[2] = {0u, 0u};
       if (nz) {
         const float inv = 127.0f / amax;
 #pragma unroll
-        for (int r = 0; r < PER; ++r) {
-          float c = rintf(x[r] * inv);
+        for (int e = 0; e < 8; ++e) {
+          float c = rintf(x[e] * inv);
           c = fminf(fmaxf(c, -127.f), 127.f);
-          sm.qc[h][lane + r * kWave] = (int8_t)(int)c;
-          qsum += (int)c;
+          const int ci = (int)c;
+          qsum += ci;
+          cw[e >> 2] |= (uint32_t)(uint8_t)(int8_t)ci << (8 * (e & 3));
         }
-      } else {
-#pragma unroll
-        for (int r = 0; r < PER; ++r) sm.qc[h][lane + r * kWave] = 0;
       }
-      qsum = wave_sum_i(qsum);
-      if (lane == 0) {
-        sm.sumq[h] = qsum;
-        sm.cq[h] = nz ? (amax / 127.0f) * p.sm_scale : 0.f;
+      *reinterpret_cast<u32x2_t*>(&sm.qc[qr][qk * 8]) = u32x2_t{cw[0], cw[1]};
+      qsum = group_sum_i<QC>(qsum);
+      if (qk == 0) {
+        sm.sumq[qr] = qsum;
+        sm.cq[qr] = nz ? (amax / 127.0f) * p.sm_scale : 0.f;
       }
     }
   }
@@ -776,7 +778,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     if (p.pm_sink_local) __syncthreads();
   }
-  if (w == 0) select_blocks<D, G, QT, DENSE>(p, sm, b, j, j0, nblk, part == 0 ? nmask : 0, sl, lane);
+  if (w == 0) select_blocks<D, G, QT, DENSE>(p, sm, b, j, j0, nblk, sl, lane);
   __syncthreads();
 
   // ---- attend -------------------------------------------------------------
@@ -827,15 +829,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     sm.rlse[h] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  for (int i = tid; i < R * D; i += kThreads) {
-    const int h = i / D, cc = i % D;
+  constexpr int D4 = D / 4;
+  for (int i = tid; i < R * D4; i += kThreads) {
+    const int h = i / D4, cc = (i % D4) * 4;
     if (h / G >= p.Q) continue;
-    float o = 0.f;
+    f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) o += sm.wo[ww][h][cc] * sm.wa[ww][h];
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sm.wo[ww][h][cc]);
+      const float a = sm.wa[ww][h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += x[e] * a;
+    }
     const size_t row = (row_index<G>(p, b, j, h) * p.n_splits + split) * p.split_parts + part;
-    p.o_part[row * D + cc] = o;
+    *reinterpret_cast<f32x4_t*>(p.o_part + row * D + cc) = o;
     if (cc == 0) p.lse_part[row] = sm.rlse[h];
+  }
+  // the split's mask entries (blocks past the sequence are 0), four per thread
+  if (p.mask != nullptr && part == 0) {
+    const int n4 = (nmask + 3) / 4;
+    for (int i = tid; i < R * n4; i += kThreads) {
+      const int r = i / n4, c = 4 * (i % n4);
+      if (r / G >= p.Q) continue;
+      uint8_t* dst = p.mask + row_index<G>(p, b, j, r) * p.nb_max + j0 + c;
+      uint32_t m4 = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m4 |= (uint32_t)((sm.hmb[min(c + e, kMaxSplit - 1)] >> r) & 1u) << (8 * e);
+      if (c + 4 <= nmask && ((uintptr_t)dst & 3u) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = m4;
+      } else {
+        for (int e = 0; e < 4 && c + e < nmask; ++e) dst[e] = (uint8_t)(m4 >> (8 * e));
+      }
+    }
   }
 }
 

@@ -52,6 +52,38 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   return x;
 }
 
+// Reductions over aligned groups of N = 8 or 16 consecutive lanes, DPP moves
+// only; every lane of a group gets its group's result (the partners of each
+// step hold equal partial results, so a float sum is the same on every lane).
+// All lanes of a group must be active.
+template <int N>
+__device__ __forceinline__ float group_max_f(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x = fmaxf(x, dpp_f<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  if constexpr (N == 16) x = fmaxf(x, dpp_f<kDppMirror>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_sum_f(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x += dpp_f<kDppQuadXor1>(x);
+  x += dpp_f<kDppQuadXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  if constexpr (N == 16) x += dpp_f<kDppMirror>(x);
+  return x;
+}
+template <int N>
+__device__ __forceinline__ int group_sum_i(int x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  x += __builtin_amdgcn_update_dpp(0, x, kDppQuadXor1, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppQuadXor2, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppHalfMirror, 0xf, 0xf, false);
+  if constexpr (N == 16) x += __builtin_amdgcn_update_dpp(0, x, kDppMirror, 0xf, 0xf, false);
+  return x;
+}
+
 // Row index (in a [rows, D] view of the cache) of token 0 of block jb of
 // sequence b, kv head j. Contiguous cache: [B, Hkv, cap, D]. Paged cache: the
 // block lives in page block_table[b, jb] of a [num_pages, Hkv, 64, D] pool;
