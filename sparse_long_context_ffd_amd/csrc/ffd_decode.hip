@@ -14,19 +14,21 @@
 // the chip, P workgroups share a split (each scans and selects all of it and
 // attends every P-th kept block).
 //
-//  prologue  the query rows -> LDS: fp32 copy and int8 copy + per-row scale
-//            (the scan query).
+//  prologue  the query rows -> LDS (one 16-byte load per thread): the bf16
+//            rows and the int8 copy + per-row scale (the scan query), reduced
+//            within the lanes holding a row.
 //  scan      each wave takes whole blocks, 16-token tiles; lane (g, n) holds
 //            D/8 bytes of int4 codes of token n (16 tokens x D/2 B = one
 //            contiguous wave load). Nibbles are moved to offset binary (x ^ 8
 //            = code + 8, 0..15) and all query rows' dots are one
-//            v_mfma_i32_16x16x64_i8 per 64 dims; the 8*sum(q) excess is
-//            subtracted after. Block score = max over valid tokens -> LDS.
+//            v_mfma_i32_16x16x64_i8 per 64 dims, tokens as rows, so a lane
+//            ends with 4 tokens of one query row; the accumulator starts at
+//            the -8*sum(q) excess. Block score = max over valid tokens -> LDS.
 //            (2-bit thumbnails: the codes spread to bytes, same MFMA.)
 //  select    wave 0: per row split max m~ (or the sink/local estimate),
-//            threshold fl32(m~ - δ), forced sink/local blocks, mask store, and
-//            a ballot-compacted list of the blocks kept by at least one row
-//            (with a per-row bit mask).
+//            threshold fl32(m~ - δ), forced sink/local blocks, and a
+//            ballot-compacted list of the blocks kept by at least one row
+//            (with a per-row bit mask); the mask is stored in the epilogue.
 //  attend    waves take kept blocks round-robin, one 64-token block at a
 //            time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the query
 //            rows padded to 16 columns):
@@ -45,6 +47,8 @@
 //            merges the splits (a merge inside this kernel needs device-scope
 //            publication of the partials, which measured slower on gfx950).
 #include <math.h>
+
+#include <type_traits>
 
 #include "ffd_device.h"
 #include "ffd_internal.h"
@@ -137,19 +141,22 @@ __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) 
 // ---------------------------------------------------------------------------
 // int4 scan: the R query rows' scores (the G heads, or G x Q for Q query
 // tokens) are one small integer matrix product per 16-token tile, done on the
-// matrix cores (v_mfma_i32_16x16x64_i8; exact int32): A = the int8 queries
-// (row n = lane % 16), B = the tile's codes moved to offset binary (code + 8,
-// token column n = lane % 16); lane group g = lane / 16 holds dims
+// matrix cores (v_mfma_i32_16x16x64_i8; exact int32): A = the tile's codes
+// moved to offset binary (code + 8, token row n = lane % 16), B = the int8
+// queries (row column n = lane % 16); lane group g = lane / 16 holds dims
 // g*D/4 .. +D/4 of both, in the order the nibbles are unpacked. Output lane
-// (g, n) holds rows 4g..4g+3 of token n; the 8*sum(q) excess is subtracted and
+// (g, n) holds tokens 4g..4g+3 of row n, so a block's max per row is a max
+// over the lane's 16 scores and then over its 4 lane groups. The accumulator
+// starts at -8*sum(q), the offset-binary excess, so it ends at the dot product;
 // s^ = fl32(float(dot) * fl32(scale * cq)). Each row only counts the tokens
-// its query token sees. (A v_dot4_i32_i8 scan, a quad of lanes per token,
-// measured slower: 371 vs 365 us at 128K x4, 45 vs 41 us at 32K.)
+// its query token sees (a mask needed only in a block that reaches past the
+// shortest row). (A v_dot4_i32_i8 scan, a quad of lanes per token, measured
+// slower: 371 vs 365 us at 128K x4, 45 vs 41 us at 32K.)
 // THUMB: the 2-bit thumbnail codes u instead ([TS] Methodology 1: the
 // thumbnails are what the scan streams): operand word e of MFMA s is
 // (codes >> 2e) & 0x03030303, whose byte m is the code of dim 16s + 4m + e;
 // dot = 2 * sum qc*u - 3 * sum qc, s^ = fl32(float(dot) * fl32(t * cq)).
-template <int D, int G, int QT, bool THUMB>
+template <int D, int G, int QT, bool THUMB, bool VEC>
 __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
                                                int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
   constexpr int R = G * QT;
@@ -157,8 +164,8 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
   const int nblk = nblk_split + nx;
   const int n = lane & 15;
   const int g = lane >> 4;
-  // A operand: word e of MFMA s holds dims g*D/4 + 8*(2s + e/2) + 2*i + (e & 1)
-  // (int4) or g*D/4 + 16s + 4i + e (thumbnail), i = 0..3
+  // B operand: word e of MFMA s holds dims g*D/4 + 8*(2s + e/2) + 2*i + (e & 1)
+  // (int4) or g*D/4 + 16s + 4i + e (thumbnail), i = 0..3, of row n
   i32x4_t qa[NM];
 #pragma unroll
   for (int s = 0; s < NM; ++s)
@@ -173,20 +180,17 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
         qa[s][e] = n < R ? pack4_i8(q8[0], q8[2], q8[4], q8[6]) : 0;
       }
     }
-  int corr[4], Lr[4];
-  float cq[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int rr = 4 * g + r;
-    corr[r] = rr < R ? (THUMB ? 3 : 8) * sm.sumq[rr] : 0;
-    cq[r] = rr < R ? sm.cq[rr] : 0.f;
-    Lr[r] = rr < R ? row_len<G>(p, sl, rr) : 0;
-  }
+  // row n's correction, scale and length (rows past R: no tokens)
+  const int corr = n < R ? (THUMB ? 3 : 8) * sm.sumq[n] : 0;
+  const float cq = n < R ? sm.cq[n] : 0.f;
+  const int Lr = n < R ? row_len<G>(p, sl, n) : 0;
+  const int Lmin = row_len<G>(p, sl, 0);   // the first query token's rows see the fewest tokens
+  const i32x4_t acc0 = THUMB ? i32x4_t{0, 0, 0, 0} : i32x4_t{-corr, -corr, -corr, -corr};
 
   constexpr int kChunk = 4;
   for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
     u32x4_t cw[kChunk][4];
-    float sc[kChunk][4];
+    f32x4_t sc[kChunk][4];   // scales of tokens 16T + 4g .. +3 of the block
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
@@ -211,7 +215,19 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
             const uint32_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src)) : 0u;
             cw[c][T] = u32x4_t{u, 0u, 0u, 0u};
           }
-          sc[c][T] = ok ? __builtin_nontemporal_load(ks + (t - t0)) : 0.f;
+        }
+        // VEC: one 16-byte load per tile (a group past the sequence reads the
+        // block's first group instead, masked below); else token by token,
+        // tokens past the sequence read as 0
+#pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          const int tl = 16 * T + 4 * g;
+          if constexpr (VEC) {
+            sc[c][T] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ks + (t0 + tl < L ? tl : 0)));
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[c][T][r] = t0 + tl + r < L ? ks[tl + r] : 0.f;
+          }
         }
       }
     }
@@ -220,53 +236,47 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
       const int jl = jc + c * kWaves;
       if (jl >= nblk) continue;
       const int t0 = (jl < nblk_split ? j0 + jl : sm.xidx[jl - nblk_split]) * kBlockSize;
-      float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      float bm = -INFINITY;
+      // scores of the block's 4 tiles; MASKED: drop the tokens row n cannot see
+      auto tiles = [&](auto masked) {
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        i32x4_t acc = i32x4_t{0, 0, 0, 0};
+        for (int T = 0; T < 4; ++T) {
+          i32x4_t acc = acc0;
 #pragma unroll
-        for (int s = 0; s < NM; ++s) {
-          i32x4_t kb;
-          if constexpr (THUMB) {
-            const uint32_t x = cw[c][T][s];
-            kb = i32x4_t{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
-                         (int)((x >> 6) & 0x03030303u)};
-          } else {
-            const uint32_t x0 = cw[c][T][2 * s] ^ 0x88888888u;   // two's complement -> code + 8
-            const uint32_t x1 = cw[c][T][2 * s + 1] ^ 0x88888888u;
-            kb = i32x4_t{(int)(x0 & 0x0f0f0f0fu), (int)((x0 >> 4) & 0x0f0f0f0fu), (int)(x1 & 0x0f0f0f0fu),
-                         (int)((x1 >> 4) & 0x0f0f0f0fu)};
+          for (int s = 0; s < NM; ++s) {
+            i32x4_t kb;
+            if constexpr (THUMB) {
+              const uint32_t x = cw[c][T][s];
+              kb = i32x4_t{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
+                           (int)((x >> 6) & 0x03030303u)};
+            } else {
+              // two's complement -> code + 8, low and high nibbles
+              const uint32_t x0 = cw[c][T][2 * s], x1 = cw[c][T][2 * s + 1];
+              kb = i32x4_t{(int)((x0 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x0 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu),
+                           (int)((x1 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x1 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu)};
+            }
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb, qa[s], acc, 0, 0, 0);
           }
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[s], kb, acc, 0, 0, 0);
-        }
-        const int t = t0 + 16 * T + n;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float wgt = sc[c][T] * cq[r];
-          const int dot = THUMB ? 2 * acc[r] - corr[r] : acc[r] - corr[r];
-          const float sv = (float)dot * wgt;
-          if (t < Lr[r]) bm[r] = fmaxf(bm[r], sv);
-        }
-      }
-      // max over the 16 token columns of each row (one DPP row of 16 lanes)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = bm[r];
-        m = fmaxf(m, dpp_f<kDppQuadXor1>(m));
-        m = fmaxf(m, dpp_f<kDppQuadXor2>(m));
-        m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
-        m = fmaxf(m, dpp_f<kDppMirror>(m));
-        bm[r] = m;
-      }
-      if (n == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rr = 4 * g + r;
-          if (rr < R) {
-            if (jl < nblk_split) sm.blk[jl][rr] = bm[r];
-            else sm.xblk[jl - nblk_split][rr] = bm[r];
+          for (int r = 0; r < 4; ++r) {
+            const float wgt = sc[c][T][r] * cq;
+            const int dot = THUMB ? 2 * acc[r] - corr : acc[r];
+            const float sv = (float)dot * wgt;
+            if constexpr (decltype(masked)::value)
+              bm = fmaxf(bm, t0 + 16 * T + 4 * g + r < Lr ? sv : -INFINITY);
+            else
+              bm = fmaxf(bm, sv);
           }
         }
+      };
+      if (t0 + kBlockSize <= Lmin) tiles(std::false_type{});
+      else tiles(std::true_type{});
+      // max over the 4 lane groups (tokens 4g..4g+3 of each tile)
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      if (g == 0 && n < R) {
+        if (jl < nblk_split) sm.blk[jl][n] = bm;
+        else sm.xblk[jl - nblk_split][n] = bm;
       }
     }
   }
@@ -758,7 +768,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // sink/local pseudo-max: the sink and local blocks outside this split are
     // listed in the prologue and scanned in the same pass as the split
     const int nx = p.pm_sink_local ? sm.nx : 0;
-    scan_blocks_mq<D, G, QT, THUMB>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
+    if (p.scale_vec)
+      scan_blocks_mq<D, G, QT, THUMB, true>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
+    else
+      scan_blocks_mq<D, G, QT, THUMB, false>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
     __syncthreads();
     // m~ per row over its own sink and local blocks: wave 0, one lane per
     // scored block (the extra ones first, then the split's), wave max per row
