@@ -25,10 +25,11 @@
 //            ends with 4 tokens of one query row; the accumulator starts at
 //            the -8*sum(q) excess. Block score = max over valid tokens -> LDS.
 //            (2-bit thumbnails: the codes spread to bytes, same MFMA.)
-//  select    wave 0: per row split max m~ (or the sink/local estimate),
-//            threshold fl32(m~ - δ), forced sink/local blocks, and a
-//            ballot-compacted list of the blocks kept by at least one row
-//            (with a per-row bit mask); the mask is stored in the epilogue.
+//  select    the waves share the rows: per row split max m~ (or the
+//            sink/local estimate), threshold fl32(m~ - δ), forced sink/local
+//            blocks; then wave 0 compacts the blocks kept by at least one row
+//            into a list (with a per-row bit mask) by ballot. The mask is
+//            stored in the epilogue.
 //  attend    waves take kept blocks round-robin, one 64-token block at a
 //            time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the query
 //            rows padded to 16 columns):
@@ -82,12 +83,12 @@ struct DecodeSmem {
   int xidx[kMaxPseudoMax];  // sink/local blocks outside the split (sink/local pseudo-max)
   int nx;
   float xblk[kMaxPseudoMax][R];
-  float pm[R];              // sink/local pseudo-max per row
   float seed[R];            // split max of the block scores (natural-log units)
   int rowp[kMaxSplit];      // paged cache: first cache row of each block of the split
   uint8_t kidx[kMaxSplit];  // kept blocks (split-local index)
   uint16_t khm[kMaxSplit];  // per-row keep bits of each kept block
   uint16_t hmb[kMaxSplit];  // per-row keep bits of every block of the split (mask)
+  uint16_t hmw[kWaves][kMaxSplit];  // the same, for the rows of each wave
   int nkept;
   float wm[kWaves][R];
   float wl[kWaves][R];
@@ -288,35 +289,53 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
 // ---------------------------------------------------------------------------
 // Row r (query token r / G, head r % G) sees NB_r blocks; a block it cannot see
 // is never kept for it, and its sink/local blocks are those of its own range.
-template <int D, int G, int QT, bool DENSE>
-__device__ __forceinline__ void select_blocks(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
-                                              int j0, int nblk, int sl, int lane) {
+// Wave w takes rows w, w + 4, ...; lane = block of the split. Per row: the
+// split max m~ (the seed of its softmax, and the pseudo-max in split mode) or
+// the sink/local estimate (max over the row's own sink and local blocks, the
+// extra ones scanned outside the split first), the threshold fl32(pm - δ),
+// the forced blocks; the row's keep bits go to LDS per wave.
+template <int D, int G, int QT>
+__device__ __forceinline__ void select_rows(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int j0, int nblk,
+                                            int nx, int sl, int lane, int w) {
   constexpr int R = G * QT;
   const int jl = lane;
   const int jb = j0 + jl;
   const bool in_split = jl < nblk;
   unsigned hm = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
+  for (int r = w; r < R; r += kWaves) {
     const int NBr = (row_len<G>(p, sl, r) + kBlockSize - 1) / kBlockSize;
-    const bool vis = in_split && jb < NBr;
-    if constexpr (DENSE) {
-      if (vis) hm |= 1u << r;
-    } else {
-      const float s = vis ? sm.blk[jl][r] : -INFINITY;
-      const bool forced = jb < p.sink || jb >= NBr - p.local;
-      const float mt = wave_max_f(s);   // split max: the pseudo-max in split mode, else the seed
-      const float pm = p.pm_sink_local ? sm.pm[r] : mt;
-      const float thr = pm - p.delta;
-      if (vis && (s >= thr || forced)) hm |= 1u << r;
-      if (lane == 0) sm.seed[r] = mt;
+    float pm = 0.f;
+    if (p.pm_sink_local) {
+      float m = -INFINITY;
+      for (int i = lane; i < nx + nblk; i += kWave) {
+        const int jx = i < nx ? sm.xidx[i] : j0 + (i - nx);
+        const float sc = i < nx ? sm.xblk[i][r] : sm.blk[i - nx][r];
+        if (jx < NBr && (jx < p.sink || jx >= NBr - p.local)) m = fmaxf(m, sc);
+      }
+      pm = wave_max_f(m);
     }
+    const bool vis = in_split && jb < NBr;
+    const float s = vis ? sm.blk[jl][r] : -INFINITY;
+    const bool forced = jb < p.sink || jb >= NBr - p.local;
+    const float mt = wave_max_f(s);
+    if (!p.pm_sink_local) pm = mt;
+    const float thr = pm - p.delta;
+    if (vis && (s >= thr || forced)) hm |= 1u << r;
+    if (lane == 0) sm.seed[r] = mt;
   }
-  sm.hmb[jl] = (uint16_t)hm;   // the mask is written in the epilogue
+  sm.hmw[w][jl] = (uint16_t)hm;
+}
+
+// The kept list (one wave, lane = block): blocks kept by at least one row,
+// compacted by ballot, each with its per-row keep bits; hm also goes to LDS
+// for the mask, which is written in the epilogue.
+template <int D, int R>
+__device__ __forceinline__ void compact_kept(DecodeSmem<D, R>& sm, unsigned hm, int lane) {
+  sm.hmb[lane] = (uint16_t)hm;
   const unsigned long long bal = __ballot(hm != 0u);
   const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
   if (hm != 0u) {
-    sm.kidx[pos] = (uint8_t)jl;
+    sm.kidx[pos] = (uint8_t)lane;
     sm.khm[pos] = (uint16_t)hm;
   }
   if (lane == 0) sm.nkept = __popcll(bal);
@@ -773,25 +792,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     else
       scan_blocks_mq<D, G, QT, THUMB, false>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
     __syncthreads();
-    // m~ per row over its own sink and local blocks: wave 0, one lane per
-    // scored block (the extra ones first, then the split's), wave max per row
-    if (p.pm_sink_local && w == 0) {
+    select_rows<D, G, QT>(p, sm, j0, nblk, nx, sl, lane, w);
+    __syncthreads();
+    if (w == 0) {
+      unsigned hm = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int NBr = (row_len<G>(p, sl, r) + kBlockSize - 1) / kBlockSize;
-        float m = -INFINITY;
-        for (int i = lane; i < nx + nblk; i += kWave) {
-          const int jb = i < nx ? sm.xidx[i] : j0 + (i - nx);
-          const float sc = i < nx ? sm.xblk[i][r] : sm.blk[i - nx][r];
-          if (jb < NBr && (jb < p.sink || jb >= NBr - p.local)) m = fmaxf(m, sc);
-        }
-        m = wave_max_f(m);
-        if (lane == 0) sm.pm[r] = m;
-      }
+      for (int ww = 0; ww < kWaves; ++ww) hm |= sm.hmw[ww][lane];
+      compact_kept(sm, hm, lane);
     }
-    if (p.pm_sink_local) __syncthreads();
+  } else {
+    // every block the row sees
+    if (w == 0) {
+      unsigned hm = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane < nblk && j0 + lane < (row_len<G>(p, sl, r) + kBlockSize - 1) / kBlockSize) hm |= 1u << r;
+      compact_kept(sm, hm, lane);
+    }
   }
-  if (w == 0) select_blocks<D, G, QT, DENSE>(p, sm, b, j, j0, nblk, sl, lane);
   __syncthreads();
 
   // ---- attend -------------------------------------------------------------
