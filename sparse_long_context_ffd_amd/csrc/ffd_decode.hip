@@ -653,21 +653,6 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
 // split combine: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s
 // ---------------------------------------------------------------------------
 
-// Natural-log normaliser over the ns split LSEs at lp (one full wave).
-__device__ __forceinline__ float merged_lse(const float* lp, int ns, int lane) {
-  float mx = -INFINITY;
-  for (int s = lane; s < ns; s += kWave) mx = fmaxf(mx, lp[s]);
-  mx = wave_max_f(mx);
-  float den = 0.f;
-  for (int s = lane; s < ns; s += kWave) {
-    const float v = lp[s];
-    den += (v == -INFINITY) ? 0.f : expf(v - mx);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-  return (ns > 0 && den > 0.f) ? mx + logf(den) : -INFINITY;
-}
-
 __device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, float v) {
   if (p.out_f32) static_cast<float*>(p.out)[idx] = v;
   else static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(v);
@@ -898,53 +883,84 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 // ---------------------------------------------------------------------------
 // split combine: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) o_s
 // ---------------------------------------------------------------------------
-// One workgroup per (query-head row, 32 output dims): wave 0 forms the merged
-// LSE over the row's partials; 8 groups of 32 threads each sum an interleaved
-// eighth of the partials (four loads in flight per thread) and the groups are
-// added in a fixed order (deterministic). Spreading a row over D/32
-// workgroups keeps the short latency chain of a long sequence's many
-// partials off one workgroup.
+// One workgroup per (query-head row, 32 output dims), one pass: 8 groups of 32
+// threads each merge an interleaved eighth of the row's partials online (a
+// running max m and sum l of exp(lse_s - m), the outputs weighted alike), with
+// the loads of up to 8 partials per thread issued before the sequence length
+// arrives (reads past the sequence's partials stay inside the row's slots and
+// are dropped); the 8 groups are then merged in a fixed order (deterministic).
+// Spreading a row over D/32 workgroups keeps the latency chain short.
 constexpr int kCombineDims = 32;
 constexpr int kCombineThreads = 256;
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const DecodeParams p) {
   constexpr int PARTS = kCombineThreads / kCombineDims;
-  __shared__ float s_lse;
+  constexpr int U = 8;   // partials per thread per step
+  __shared__ float gm[PARTS], gl[PARTS];
   __shared__ float red[PARTS][kCombineDims];
   const int h = blockIdx.x, b = blockIdx.y, c0 = blockIdx.z * kCombineDims, tid = threadIdx.x;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
-  const int NB = (L + kBlockSize - 1) / kBlockSize;
-  const int ns = (NB + p.split_blocks - 1) / p.split_blocks * p.split_parts;   // partials of this sequence
-  const size_t bh = (size_t)b * p.Q * p.Hq + h;   // row (b, query token h / Hq, head h % Hq)
-  const size_t per_row = (size_t)p.n_splits * p.split_parts;
-  const float* lp = p.lse_part + bh * per_row;
-  const float* op = p.o_part + bh * per_row * D + c0;
-  if (tid < kWave) {
-    const float l = merged_lse(lp, ns, tid);
-    if (tid == 0) s_lse = l;
-  }
-  __syncthreads();
-  const float lse = s_lse;
   const int c = tid % kCombineDims, part = tid / kCombineDims;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (lse != -INFINITY) {
-    int s = part;
-    for (; s + 3 * PARTS < ns; s += 4 * PARTS) {
+  const size_t bh = (size_t)b * p.Q * p.Hq + h;   // row (b, query token h / Hq, head h % Hq)
+  const int per_row = p.n_splits * p.split_parts;
+  const float* lp = p.lse_part + bh * per_row;
+  const float* op = p.o_part + bh * per_row * D + c0 + c;
+  int L = p.seq_lens[b];
+  float m = -INFINITY, l = 0.f, acc = 0.f;
+  for (int s0 = part; s0 < per_row; s0 += U * PARTS) {
+    float lv[U], ov[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] += expf(lp[s + u * PARTS] - lse) * op[(size_t)(s + u * PARTS) * D + c];
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * PARTS;
+      lv[u] = s < per_row ? lp[s] : -INFINITY;
+      ov[u] = s < per_row ? op[(size_t)s * D] : 0.f;
     }
-    for (; s < ns; s += PARTS) acc[0] += expf(lp[s] - lse) * op[(size_t)s * D + c];
+    L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+    const int NB = (L + kBlockSize - 1) / kBlockSize;
+    const int ns = (NB + p.split_blocks - 1) / p.split_blocks * p.split_parts;   // partials of this sequence
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u * PARTS >= ns) lv[u] = -INFINITY;   // slots past the sequence's partials
+      mx = fmaxf(mx, lv[u]);
+    }
+    if (mx == -INFINITY) continue;   // nothing seen yet
+    const float a = (m == -INFINITY) ? 0.f : expf(m - mx);
+    l *= a;
+    acc *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // an empty partial (or an unwritten slot) adds nothing, whatever it holds
+      if (lv[u] != -INFINITY) {
+        const float wt = expf(lv[u] - mx);
+        l += wt;
+        acc += wt * ov[u];
+      }
+    }
+    m = mx;
   }
-  red[part][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  red[part][c] = acc;
+  if (c == 0) {
+    gm[part] = m;
+    gl[part] = l;
+  }
   __syncthreads();
   if (part == 0) {
-    float res = 0.f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < PARTS; ++q) res += red[q][c];
-    store_out(p, bh * D + c0 + c, res);
-    if (c0 == 0 && c == 0) p.lse[bh] = lse;
+    for (int q = 0; q < PARTS; ++q) M = fmaxf(M, gm[q]);
+    float den = 0.f, res = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) {
+        const float a = (gm[q] == -INFINITY) ? 0.f : expf(gm[q] - M);
+        den += gl[q] * a;
+        res += red[q][c] * a;
+      }
+    }
+    const bool any = den > 0.f;
+    store_out(p, bh * D + c0 + c, any ? res / den : 0.f);
+    if (c0 == 0 && c == 0) p.lse[bh] = any ? M + logf(den) : -INFINITY;
   }
 }
 
