@@ -9,9 +9,9 @@ import pytest
 import torch
 
 import sparse_long_context_ffd_amd as ffd
-from ffd_inputs import WORKLOADS, make_inputs, make_random_inputs
+from ffd_inputs import WORKLOADS, make_inputs, make_random_inputs, multi_query
 from oracle import ffd_oracle as O
-from tests.gpu_util import assert_close, assert_mask_equal, run_gpu, say, sm_scale_for, to_device
+from tests.gpu_util import assert_close, assert_mask_equal, dev_bf16, run_gpu, say, sm_scale_for, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +189,40 @@ def test_workspace_reused_across_calls_with_different_lengths():
         assert_mask_equal(a[2].cpu().numpy(), r_mask, f"mask {lens}")
         assert_close(a[0].cpu().numpy(), r_out, f"out {lens}")
         assert_close(a[1].cpu().numpy(), r_lse, f"lse {lens}")
+
+
+def test_workspace_garbage_is_never_used():
+    """The combine reads each row's partial slots past the sequence's own
+    (they lie inside the row's workspace) and drops them: a workspace full of
+    NaN bytes gives bit-identical results to a zeroed one, for rows with no
+    tokens, short rows and long rows (several query tokens too)."""
+    say("decode: NaN-filled workspace")
+    lens = (6000, 0, 130, 64 * 32 * 3)
+    inp = make_random_inputs(4, 16, 4, 128, lens, seed=51, block_size=64)
+    dv = to_device(inp)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    res = []
+    for fill in (0x00, 0xFF):
+        ws = ffd.alloc_workspace(4, 16, 128, inp["cap"], 64, 8)
+        ws.fill_(fill)
+        res.append(ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], delta=1.5, split_blocks=8,
+                              workspace=ws, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for a, b, what in zip(res[0], res[1], ("out", "lse", "mask")):
+        assert torch.equal(a, b), what
+    assert not torch.isnan(res[1][0]).any() and not torch.isnan(res[1][1]).any()
+    assert torch.isneginf(res[1][1][1]).all() and (res[1][0][1] == 0).all()
+    Q = 3
+    qm = dev_bf16(multi_query(inp, Q, seed=52))
+    res = []
+    for fill in (0x00, 0xFF):
+        ws = torch.full((ffd.ffd_decode_multi_workspace_bytes(4, Q, 16, 128, inp["cap"], 64, 8),), fill,
+                        dtype=torch.uint8, device="cuda")
+        res.append(ffd.decode_multi(qm, dv["k"], dv["v"], kq, ks, dv["seq_lens"], delta=1.5, split_blocks=8,
+                                    workspace=ws, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for a, b, what in zip(res[0], res[1], ("out", "lse", "mask")):
+        assert torch.equal(a, b), "multi " + what
 
 
 def test_graph_capture_and_replay():
