@@ -124,8 +124,8 @@ __device__ __forceinline__ int row_len(const DecodeParams& p, int sl, int r) {
 // First cache row of block jb of (sequence b, kv head j). For a paged cache
 // the split's rows were looked up once into LDS (rowp); blocks outside the
 // split (sink/local pseudo-max) read the block table directly.
-template <int D, int G>
-__device__ __forceinline__ size_t block_row(const DecodeParams& p, const DecodeSmem<D, G>& sm, int b, int j, int j0,
+template <int D, int R>
+__device__ __forceinline__ size_t block_row(const DecodeParams& p, const DecodeSmem<D, R>& sm, int b, int j, int j0,
                                             int nblk, int jb) {
   if (p.block_table != nullptr && jb >= j0 && jb < j0 + nblk) return (size_t)(unsigned)sm.rowp[jb - j0] * kBlockSize;
   return cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
@@ -385,8 +385,8 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const char* p) {
       reinterpret_cast<bf16x4_t __attribute__((address_space(3)))*>((__attribute__((address_space(3))) char*)p));
 }
 
-// Per-wave online-softmax state of the attend phase. Lane l serves query head
-// h = l % 16 (rows h >= G are padding) for the tokens 4*(l/16)..+3 of every
+// Per-wave online-softmax state of the attend phase. Lane l serves query row
+// h = l % 16 (rows h >= R are padding) for the tokens 4*(l/16)..+3 of every
 // 16-token tile; o[nt][r] holds output row 4*(l/16)+r, column 16*nt + l%16.
 template <int D>
 struct AttendState {
