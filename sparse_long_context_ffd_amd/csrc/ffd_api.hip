@@ -237,9 +237,6 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.sink = sink_blocks;
   p.local = local_blocks;
   p.pm_sink_local = pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL;
-  // the scan reads 4 scales per 16-byte load when each block's scales start
-  // 16-byte aligned and a 4-token group never runs past its row (pages hold 64)
-  p.scale_vec = aligned16(kscale) && (block_table != nullptr || cap % 4 == 0);
   p.delta = delta;
   p.sm_scale = sm_scale;
   return FFD_OK;

@@ -157,7 +157,7 @@ __device__ __forceinline__ int pack4_i8(int8_t a, int8_t b, int8_t c, int8_t d) 
 // thumbnails are what the scan streams): operand word e of MFMA s is
 // (codes >> 2e) & 0x03030303, whose byte m is the code of dim 16s + 4m + e;
 // dot = 2 * sum qc*u - 3 * sum qc, s^ = fl32(float(dot) * fl32(t * cq)).
-template <int D, int G, int QT, bool THUMB, bool VEC>
+template <int D, int G, int QT, bool THUMB>
 __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
                                                int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
   constexpr int R = G * QT;
@@ -191,7 +191,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
   constexpr int kChunk = 4;
   for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
     u32x4_t cw[kChunk][4];
-    f32x4_t sc[kChunk][4];   // scales of tokens 16T + 4g .. +3 of the block
+    float scl[kChunk];   // lane (g, n): scale of token 16 * (n / 4) + 4g + n % 4 of the block
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
       const int jl = jc + c * kWaves;
@@ -217,19 +217,11 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
             cw[c][T] = u32x4_t{u, 0u, 0u, 0u};
           }
         }
-        // VEC: one 16-byte load per tile (a group past the sequence reads the
-        // block's first group instead, masked below); else token by token,
-        // tokens past the sequence read as 0
-#pragma unroll
-        for (int T = 0; T < 4; ++T) {
-          const int tl = 16 * T + 4 * g;
-          if constexpr (VEC) {
-            sc[c][T] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ks + (t0 + tl < L ? tl : 0)));
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[c][T][r] = t0 + tl + r < L ? ks[tl + r] : 0.f;
-          }
-        }
+        // the 16 scales lane (g, n) needs (tokens 16T + 4g + r) are held by
+        // lanes 4T + r of its own 16-lane row: one load per lane, then row
+        // broadcasts; tokens past the sequence are not read
+        const int tl = 16 * (n >> 2) + 4 * g + (n & 3);
+        scl[c] = t0 + tl < L ? __builtin_nontemporal_load(ks + tl) : 0.f;
       }
     }
 #pragma unroll
@@ -260,7 +252,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float wgt = sc[c][T][r] * cq;
+            const float wgt = row_bcast_f(scl[c], 4 * T + r) * cq;
             const int dot = THUMB ? 2 * acc[r] - corr : acc[r];
             const float sv = (float)dot * wgt;
             if constexpr (decltype(masked)::value)
@@ -772,10 +764,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // sink/local pseudo-max: the sink and local blocks outside this split are
     // listed in the prologue and scanned in the same pass as the split
     const int nx = p.pm_sink_local ? sm.nx : 0;
-    if (p.scale_vec)
-      scan_blocks_mq<D, G, QT, THUMB, true>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
-    else
-      scan_blocks_mq<D, G, QT, THUMB, false>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
+    scan_blocks_mq<D, G, QT, THUMB>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
     __syncthreads();
     select_rows<D, G, QT>(p, sm, j0, nblk, nx, sl, lane, w);
     __syncthreads();

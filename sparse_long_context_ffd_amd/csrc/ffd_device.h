@@ -24,7 +24,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // ---- DPP lane exchanges (all 64 lanes must be active) ----------------------
 // quad_perm [1,0,3,2] and [2,3,0,1]; row_half_mirror (lane i <-> 7-i within
-// each 8-lane half row); row_mirror (lane i <-> 15-i within each 16-lane row).
+// each 8-lane half row); row_mirror (lane i <-> 15-i within each 16-lane row);
+// row_newbcast:k (lane k of each 16-lane row to the whole row).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -33,6 +34,30 @@ constexpr int kDppQuadXor1 = 0xb1;
 constexpr int kDppQuadXor2 = 0x4e;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+constexpr int kDppRowBcast0 = 0x150;   // row_newbcast:k = 0x150 + k (gfx90a and later)
+
+// Lane k (0..15) of each 16-lane row, to every lane of that row. k must fold
+// to a constant (an unrolled loop index): the switch then leaves one DPP move.
+__device__ __forceinline__ float row_bcast_f(float x, int k) {
+  switch (k) {
+    case 0: return dpp_f<kDppRowBcast0 + 0>(x);
+    case 1: return dpp_f<kDppRowBcast0 + 1>(x);
+    case 2: return dpp_f<kDppRowBcast0 + 2>(x);
+    case 3: return dpp_f<kDppRowBcast0 + 3>(x);
+    case 4: return dpp_f<kDppRowBcast0 + 4>(x);
+    case 5: return dpp_f<kDppRowBcast0 + 5>(x);
+    case 6: return dpp_f<kDppRowBcast0 + 6>(x);
+    case 7: return dpp_f<kDppRowBcast0 + 7>(x);
+    case 8: return dpp_f<kDppRowBcast0 + 8>(x);
+    case 9: return dpp_f<kDppRowBcast0 + 9>(x);
+    case 10: return dpp_f<kDppRowBcast0 + 10>(x);
+    case 11: return dpp_f<kDppRowBcast0 + 11>(x);
+    case 12: return dpp_f<kDppRowBcast0 + 12>(x);
+    case 13: return dpp_f<kDppRowBcast0 + 13>(x);
+    case 14: return dpp_f<kDppRowBcast0 + 14>(x);
+    default: return dpp_f<kDppRowBcast0 + 15>(x);
+  }
+}
 
 // Max over the wave; every lane gets it. The steps inside each 16-lane row are
 // DPP moves (VALU latency), only the two steps across rows go through LDS.

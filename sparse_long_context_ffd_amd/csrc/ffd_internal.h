@@ -54,7 +54,6 @@ struct DecodeParams {
   int split_blocks;
   int sink, local;
   int pm_sink_local;       // 1: pseudo-max over the sink/local blocks; 0: split max
-  int scale_vec;           // 1: every scan scale row is 16-byte aligned with whole 4-token groups
   float delta, sm_scale;
 };
 

@@ -1,8 +1,9 @@
-"""The scan reads the per-token key scales four at a time (one 16-byte load)
-when every scale row starts 16-byte aligned and holds whole 4-token groups, and
-token by token otherwise: a cache capacity that is not a multiple of 4, or a
-scale array that starts off a 16-byte boundary. Both ways must keep exactly
-the oracle's blocks, and the two must agree bit for bit on the same cache."""
+"""Scale layouts the scan must read correctly: each lane loads one per-token
+key scale of a block (tokens past the sequence are not read) and the others
+come by lane broadcasts. A cache capacity that is not a multiple of 4 (the last
+block runs past the rows), a scale array 4 bytes off a 16-byte boundary, and
+blocks past the capacity must keep exactly the oracle's blocks, and aligned
+and misaligned copies of one cache must agree bit for bit."""
 
 import math
 
@@ -77,8 +78,8 @@ def test_scale_layouts_match_oracle(case):
 
 
 def test_scale_loads_agree_bit_for_bit():
-    """The same cache with aligned scales (4 per load) and with the scales one
-    float off a 16-byte boundary (token by token): identical results."""
+    """The same cache with aligned scales and with the scales one float off a
+    16-byte boundary: identical results."""
     B, Hq, Hkv, d, lens, cap = 2, 16, 4, 128, (4096, 2500), 4096
     say("scale loads: aligned vs misaligned, bit for bit")
     inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=777, block_size=64, hot_frac=0.05)
