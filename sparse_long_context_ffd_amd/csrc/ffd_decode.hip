@@ -496,16 +496,14 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       tsl = p.k2scale[r0 + tl];
       s8l = p.krscale[r0 + tl];
     }
-    // The thumbnail QK holds more registers (two accumulators, operand
-    // conversion), so only a quarter of V is in flight across it: the whole
-    // tile would cost the second wave per SIMD. (Loading V straight into LDS
-    // with global_load_lds_dwordx4 frees those registers, but the compiler
-    // then waits for every outstanding load, the V DMA included, before the
-    // first use of the codes, which serialises V behind QK: slower.)
-    constexpr int VH = THUMB ? VL / 4 : VL;
+    // The whole V tile is in flight across QK, on the thumbnail path too.
+    // (Loading V straight into LDS with global_load_lds_dwordx4 frees its
+    // registers, but the compiler then waits for every outstanding load, the
+    // V DMA included, before the first use of the codes, which serialises V
+    // behind QK: slower.)
     u32x4_t vr[VL];
 #pragma unroll
-    for (int n = 0; n < VH; ++n) {
+    for (int n = 0; n < VL; ++n) {
       const int f = n * kWave + lane;        // chunk id within the tile
       const int r = f / VC, q = f % VC;
       const int t = min(t0 + r, tlast);
@@ -564,14 +562,6 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
         }
         __builtin_amdgcn_sched_barrier(0);   // convert tile by tile: bounds live registers
       }
-    }
-
-#pragma unroll
-    for (int n = VH; n < VL; ++n) {
-      const int f = n * kWave + lane;        // chunk id within the tile
-      const int r = f / VC, q = f % VC;
-      const int t = min(t0 + r, tlast);
-      vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)(t - t0) * D + q * 8));
     }
 
     // ---- V tile to LDS (this wave's region) ----
