@@ -4,7 +4,7 @@ thumbnail storage, paged cache, several query tokens), group size, head dim,
 split size up to its maximum of 64 blocks, sink/local counts up to the
 sink/local mode's limit, δ from 0 to +inf, both pseudo-max modes, bf16 and
 fp32 output, lengths that are empty, a single token, on block boundaries or
-ragged."""
+ragged, and cache capacities that are not a whole number of blocks."""
 
 import math
 
@@ -52,8 +52,19 @@ def _case(i):
     if pm == "sink_local" and sink + local == 0:
         local = 1
     out_bf16 = bool(rng.random() < 0.25)
+    # (drawn last, so the draws above are those of the earlier sweep)
+    odd_cap = bool(rng.random() < 0.3) and kind != "paged"
+    cap_extra = int(rng.integers(0, 6))
     return dict(kind=kind, B=B, Hq=G * Hkv, Hkv=Hkv, d=d, Q=Q, lens=tuple(lens), S=S, delta=delta, pm=pm,
-                sink=sink, local=local, out_bf16=out_bf16, seed=30_000 + i)
+                sink=sink, local=local, out_bf16=out_bf16, odd_cap=odd_cap, cap_extra=cap_extra, seed=30_000 + i)
+
+
+def _recap(x: torch.Tensor, cap: int) -> torch.Tensor:
+    """Cache rows [B, Hkv, cap0, d] cut, or padded with NaN, to cap rows."""
+    if cap <= x.shape[2]:
+        return x[:, :, :cap].contiguous()
+    pad = torch.full(x.shape[:2] + (cap - x.shape[2],) + x.shape[3:], float("nan"), dtype=x.dtype, device=x.device)
+    return torch.cat([x, pad], dim=2)
 
 
 def _pages(x, nbs, table_np, num_pages):
@@ -77,6 +88,10 @@ def test_random_case(i):
                              hot_frac=0.08)
     dv = to_device(inp)
     cap = inp["cap"]
+    if c["odd_cap"]:
+        # a capacity that is not a whole number of blocks (or of 4-token groups)
+        cap = max(max(c["lens"]), 1) + c["cap_extra"]
+        dv["k"], dv["v"] = _recap(dv["k"], cap), _recap(dv["v"], cap)
     sm = sm_scale_for(c["d"])
     odt = torch.bfloat16 if c["out_bf16"] else torch.float32
     kw = dict(max_seq_len=cap, block_size=64, delta=c["delta"], sink=c["sink"], local=c["local"],
