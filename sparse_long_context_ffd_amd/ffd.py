@@ -5,11 +5,15 @@ kernels behind the C ABI declared in ``include/ffd.h``. PyTorch supplies device
 memory and the current HIP stream. If the library has not been built this
 module raises on first use; there is no fallback.
 
-Low-level entry points keep the C names (``ffd_quantize_kv``, ``ffd_decode``,
-``ffd_decode_partials``, ``ffd_combine``,
-``ffd_decode_workspace_bytes``, ``ffd_last_error``, ``ffd_abi_version``) and
-take preallocated tensors. ``quantize_kv`` and ``decode`` are conveniences
-that allocate the outputs and the workspace with torch and then call them.
+Low-level entry points keep the C names (every name in ``EXPORTED_SYMBOLS``:
+the int4 sketch ``ffd_quantize_kv`` / ``ffd_decode`` and its halves
+``ffd_decode_partials`` / ``ffd_combine``, the thumbnail storage
+``ffd_quantize_kv_thumb`` / ``ffd_decode_thumb``, the paged cache
+``ffd_quantize_kv_paged`` / ``ffd_decode_paged``, several query tokens
+``ffd_decode_multi``, the workspace sizes, ``ffd_last_error`` and
+``ffd_abi_version``) and take preallocated tensors. ``quantize_kv``,
+``quantize_kv_thumb``, ``decode`` and ``decode_multi`` are conveniences that
+allocate the outputs and the workspace with torch and then call them.
 """
 
 from __future__ import annotations
