@@ -36,7 +36,8 @@ extern "C" {
 typedef enum {
   FFD_OK = 0,
   FFD_ERR_INVALID_ARG = 1, /* null pointer, inconsistent shape, bad scalar, misaligned pointer */
-  FFD_ERR_UNSUPPORTED = 2, /* valid request the kernels do not implement (d, block size, G, G*Q, S, sink+local) */
+  FFD_ERR_UNSUPPORTED = 2, /* valid request the kernels do not implement (d, block size, G, G*Q, S, sink+local,
+                              more than 2^30 tokens in max_seq_len, cap or max_span) */
   FFD_ERR_WORKSPACE = 3,   /* workspace smaller than ffd_decode_workspace_bytes() */
   FFD_ERR_HIP = 4          /* a HIP launch error */
 } ffd_status;
@@ -84,7 +85,8 @@ const char* ffd_last_error(void);
  * Build a prefix with begin = 0, end = len; append one decoded token with
  * begin = len - 1, end = len (after writing its bf16 K/V row). Both give the
  * same bytes for the same token.
- * Supported: d in {64, 128}. kq and k must be 16-byte aligned.
+ * Supported: d in {64, 128}; cap, max_span <= 2^30. kq and k must be 16-byte
+ * aligned.
  */
 ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale,
                            const int32_t* pos_begin, const int32_t* pos_end,
@@ -97,6 +99,7 @@ ffd_status ffd_quantize_kv(const void* k, uint8_t* kq, float* kscale,
  * 64]. Token t of sequence b lives in page block_table[b * table_stride + t/64]
  * (int32, device), row t % 64. Tokens at or past table_stride * 64 are not
  * processed; page numbers outside [0, num_pages) are clamped (never fault).
+ * table_stride <= 2^24.
  * Same arithmetic and output bytes as ffd_quantize_kv.
  */
 ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* kscale_pages,
@@ -188,8 +191,9 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  * A sequence with L == 0 gives out = 0, lse = -INFINITY and a zero mask row.
  * With FFD_PSEUDO_MAX_SINK_LOCAL a split may keep no block of a head; its
  * partial then has lse = -INFINITY and weight 0 in the combine.
- * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8}.
- * q, k, v, kq must be 16-byte aligned. Equivalent to ffd_decode_partials
+ * Supported: d in {64, 128}, block_size == 64, Hq / Hkv in {1, 2, 4, 8},
+ * max_seq_len <= 2^30. q, k, v, kq must be 16-byte aligned. Equivalent to
+ * ffd_decode_partials
  * followed by ffd_combine on the same stream.
  */
 ffd_status ffd_decode(const void* q, const void* k, const void* v,
@@ -303,7 +307,8 @@ ffd_status ffd_decode_partials(const void* q, const void* k, const void* v,
  * over the splits written by ffd_decode_partials (same seq_lens,
  * max_seq_len, block_size and split_blocks; workspace laid out as described
  * there). A sequence with L == 0 gives out = 0 and lse = -INFINITY.
- * Supported: d in {64, 128}, block_size == 64, split_blocks in [1, 64].
+ * Supported: d in {64, 128}, block_size == 64, split_blocks in [1, 64],
+ * max_seq_len <= 2^30.
  */
 ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, int d,
                        int block_size, int split_blocks, const void* workspace,

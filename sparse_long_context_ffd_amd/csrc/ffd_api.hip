@@ -30,9 +30,14 @@ ffd_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Longest max_seq_len, cap or max_span accepted: token positions and block
+// counts (plus a block or a workgroup's rows) then stay inside int everywhere.
+constexpr int kMaxTokens = 1 << 30;
+
+int nb_max_for(int max_seq_len) { return (int)(((long)max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize); }
+
 int n_splits_for(int max_seq_len, int split_blocks) {
-  const int nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
-  return (nb_max + split_blocks - 1) / split_blocks;
+  return (int)(((long)nb_max_for(max_seq_len) + split_blocks - 1) / split_blocks);
 }
 
 // Workspace of a decode over B sequences with `rows` query-head rows each
@@ -66,6 +71,8 @@ ffd_status quantize_common(const char* fn, const void* k, uint8_t* kq, float* ks
   if (!k || !kq || !kscale || !pos_begin || !pos_end) return fail(FFD_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   if (!aligned16(k) || !aligned16(kq)) return fail(FFD_ERR_INVALID_ARG, "%s: k and kq must be 16-byte aligned", fn);
   if (B > 65535 || Hkv > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B and Hkv must be <= 65535", fn);
+  if (max_span > kMaxTokens || cap > kMaxTokens)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: cap and max_span must be <= 2^30 tokens", fn);
   hipError_t e = ffd::launch_quantize_kv(static_cast<const uint16_t*>(k), kq, kscale, pos_begin, pos_end, block_table,
                                          table_stride, num_pages, B, Hkv, cap, d, max_span,
                                          static_cast<hipStream_t>(stream));
@@ -98,6 +105,8 @@ ffd_status ffd_quantize_kv_thumb(const void* k, uint8_t* k2, float* k2scale, int
   if (!aligned16(k) || !aligned16(k2) || !aligned16(kr))
     return fail(FFD_ERR_INVALID_ARG, "%s: k, k2, kr must be 16-byte aligned", fn);
   if (B > 65535 || Hkv > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B and Hkv must be <= 65535", fn);
+  if (max_span > kMaxTokens || cap > kMaxTokens)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: cap and max_span must be <= 2^30 tokens", fn);
   hipError_t e = ffd::launch_quantize_thumb(static_cast<const uint16_t*>(k), k2, k2scale, kr, krscale, pos_begin,
                                             pos_end, B, Hkv, cap, d, max_span, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FFD_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -113,6 +122,8 @@ ffd_status ffd_quantize_kv_paged(const void* k_pages, uint8_t* kq_pages, float* 
     return fail(FFD_ERR_INVALID_ARG, "%s: negative table_stride/num_pages (%d, %d)", fn, table_stride, num_pages);
   if (B > 0 && Hkv > 0 && max_span > 0 && table_stride > 0 && num_pages > 0 && !block_table)
     return fail(FFD_ERR_INVALID_ARG, "%s: null block_table", fn);
+  if (table_stride > kMaxTokens / ffd::kBlockSize)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: table_stride=%d above 2^24 pages per sequence", fn, table_stride);
   if (table_stride == 0 || num_pages == 0) {   // nothing addressable
     if (B < 0 || Hkv < 0 || max_span < 0) return fail(FFD_ERR_INVALID_ARG, "%s: negative size", fn);
     return ok();
@@ -125,11 +136,13 @@ size_t ffd_decode_multi_workspace_bytes(int B, int Q, int Hq, int d, int max_seq
                                         int split_blocks) {
   if (Q <= 0 || Hq <= 0 || (long)Q * Hq > 65535) return 0;
   if (B <= 0 || d <= 0 || max_seq_len <= 0 || block_size != ffd::kBlockSize || split_blocks < 1) return 0;
+  if (max_seq_len > kMaxTokens) return 0;
   return decode_ws_bytes(B, Q * Hq, Hq, max_seq_len, split_blocks, d);
 }
 
 size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int block_size, int split_blocks) {
   if (B <= 0 || Hq <= 0 || d <= 0 || max_seq_len <= 0 || block_size != ffd::kBlockSize || split_blocks < 1) return 0;
+  if (max_seq_len > kMaxTokens) return 0;
   return decode_ws_bytes(B, Hq, Hq, max_seq_len, split_blocks, d);
 }
 
@@ -151,6 +164,8 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
                 cap, max_seq_len);
   if (Hq % Hkv) return fail(FFD_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (d <= 0 || (d & 1)) return fail(FFD_ERR_INVALID_ARG, "%s: d must be positive and even (d=%d)", fn, d);
+  if (max_seq_len > kMaxTokens)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: max_seq_len=%d above 2^30 tokens", fn, max_seq_len);
   if (block_table == nullptr && cap < max_seq_len)
     return fail(FFD_ERR_INVALID_ARG, "%s: cap=%d < max_seq_len=%d", fn, cap, max_seq_len);
   if (block_table != nullptr) {
@@ -196,7 +211,7 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kq))
       return fail(FFD_ERR_INVALID_ARG, "%s: q, k, v, kq must be 16-byte aligned", fn);
   }
-  const int nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
+  const int nb_max = nb_max_for(max_seq_len);
   const int ns = max_seq_len > 0 ? n_splits_for(max_seq_len, split_blocks) : 0;
   const int rows = Q * Hq;   // query-head rows per sequence
   const int parts = ns > 0 ? ffd::split_parts_for(B, Hq, ns) : 1;
@@ -403,6 +418,8 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   if (split_blocks > ffd::kMaxSplit)
     return fail(FFD_ERR_UNSUPPORTED, "%s: split_blocks=%d not supported (<= %d)", fn, split_blocks, ffd::kMaxSplit);
   if (B > 65535 || Hq > 65535) return fail(FFD_ERR_UNSUPPORTED, "%s: B, Hq must be <= 65535", fn);
+  if (max_seq_len > kMaxTokens)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: max_seq_len=%d above 2^30 tokens", fn, max_seq_len);
   ffd_status st = check_out_dtype(fn, out_dtype);
   if (st != FFD_OK) return st;
   st = check_out_ptrs(fn, B, out, lse);
@@ -434,7 +451,7 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   p.Q = 1;
   p.Hq = Hq;
   p.Hkv = 1;
-  p.nb_max = (max_seq_len + ffd::kBlockSize - 1) / ffd::kBlockSize;
+  p.nb_max = nb_max_for(max_seq_len);
   p.n_splits = ns;
   p.split_parts = parts;
   p.split_blocks = split_blocks;

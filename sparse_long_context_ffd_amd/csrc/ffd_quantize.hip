@@ -54,16 +54,17 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
   int begin = pos_begin[b];
   int end = pos_end[b];
   begin = begin < 0 ? 0 : begin;
-  const int limit = block_table ? table_stride * 64 : cap;
+  const int limit = block_table ? table_stride * 64 : cap;   // <= 2^30 (checked on the host)
   end = end > limit ? limit : end;
-  const int t_base = begin + blockIdx.x * TPB * kRowsPerThread + tid / LPT;
+  // 64-bit: begin is a device value (unchecked), and may sit near INT_MAX
+  const long long t_base = (long long)begin + (long long)blockIdx.x * TPB * kRowsPerThread + tid / LPT;
 
   u32x4q_t w[kRowsPerThread];
   size_t row[kRowsPerThread];
 #pragma unroll
   for (int u = 0; u < kRowsPerThread; ++u) {
-    const int t = t_base + u * TPB;
-    const int tv = t < end ? t : 0;
+    const long long t = t_base + u * TPB;
+    const int tv = t < end ? (int)t : 0;
     row[u] = cache_block_row(block_table, table_stride, num_pages, cap, Hkv, b, j, tv / 64) + tv % 64;
     w[u] = t < end ? __builtin_nontemporal_load(reinterpret_cast<const u32x4q_t*>(k + row[u] * D + sub * 8))
                    : u32x4q_t{0u, 0u, 0u, 0u};
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void quantize_kv_kernel(const uint16_t* __rest
         packed |= ((uint32_t)(int)c & 0xfu) << (4 * i);
       }
     }
-    if (t_base + u * TPB < end) {
+    if (t_base + u * TPB < (long long)end) {
       *reinterpret_cast<uint32_t*>(kq + row[u] * (D / 2) + sub * 4) = packed;
       if (sub == 0) kscale[row[u]] = scale;
     }
@@ -100,7 +101,7 @@ hipError_t launch_quantize_kv(const uint16_t* k, uint8_t* kq, float* kscale, con
                               const int32_t* pos_end, const int32_t* block_table, int table_stride, int num_pages,
                               int B, int Hkv, int cap, int D, int max_span, hipStream_t stream) {
   const int rows = 256 / (D / 8) * kRowsPerThread;   // token rows per workgroup
-  dim3 grid((max_span + rows - 1) / rows, Hkv, B);
+  dim3 grid((unsigned)(((long)max_span + rows - 1) / rows), Hkv, B);
   if (D == 128) {
     quantize_kv_kernel<128><<<grid, 256, 0, stream>>>(k, kq, kscale, pos_begin, pos_end, block_table, table_stride,
                                                       num_pages, Hkv, cap);
@@ -141,20 +142,21 @@ __global__ __launch_bounds__(256) void quantize_thumb_kernel(const uint16_t* __r
   int end = pos_end[b];
   begin = begin < 0 ? 0 : begin;
   end = end > cap ? cap : end;
-  const int t_base = begin + blockIdx.x * TPB * kRowsPerThread + tid / LPT;
+  // 64-bit: begin is a device value (unchecked), and may sit near INT_MAX
+  const long long t_base = (long long)begin + (long long)blockIdx.x * TPB * kRowsPerThread + tid / LPT;
 
   u32x4q_t w[kRowsPerThread];
 #pragma unroll
   for (int u = 0; u < kRowsPerThread; ++u) {
-    const int t = t_base + u * TPB;
-    const size_t row = ((size_t)b * Hkv + j) * cap + (t < end ? t : 0);
+    const long long t = t_base + u * TPB;
+    const size_t row = ((size_t)b * Hkv + j) * cap + (t < end ? (int)t : 0);
     w[u] = t < end ? __builtin_nontemporal_load(reinterpret_cast<const u32x4q_t*>(k + row * D + sub * 8))
                    : u32x4q_t{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < kRowsPerThread; ++u) {
-    const int t = t_base + u * TPB;
-    const size_t row = ((size_t)b * Hkv + j) * cap + (t < end ? t : 0);
+    const long long t = t_base + u * TPB;
+    const size_t row = ((size_t)b * Hkv + j) * cap + (t < end ? (int)t : 0);
     float x[8];
     unpack_bf16x8(w[u], x);
     float amax = 0.f;
@@ -207,7 +209,7 @@ hipError_t launch_quantize_thumb(const uint16_t* k, uint8_t* k2, float* k2scale,
                                  const int32_t* pos_begin, const int32_t* pos_end, int B, int Hkv, int cap, int D,
                                  int max_span, hipStream_t stream) {
   const int rows = 256 / (D / 8) * kRowsPerThread;   // token rows per workgroup
-  dim3 grid((max_span + rows - 1) / rows, Hkv, B);
+  dim3 grid((unsigned)(((long)max_span + rows - 1) / rows), Hkv, B);
   if (D == 128) {
     quantize_thumb_kernel<128><<<grid, 256, 0, stream>>>(k, k2, k2scale, kr, krscale, pos_begin, pos_end, Hkv, cap);
   } else if (D == 64) {

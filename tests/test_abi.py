@@ -174,3 +174,23 @@ def test_multi_workspace_covers_every_query_row():
     assert _decode_multi(**common, ws_bytes=one, Q=2) == ffd.FFD_ERR_WORKSPACE
     assert _decode_multi(**common, ws_bytes=one, Q=4, pm=1, sink=0, local=0) == ffd.FFD_ERR_INVALID_ARG
     assert _decode_multi(B=0, Q=4) == ffd.FFD_OK
+
+
+def test_token_counts_above_2_30_are_rejected_not_overflowed():
+    """Block counts and grid sizes are computed without int overflow; lengths
+    past 2^30 tokens are refused before anything is launched."""
+    big = 2 ** 31 - 1
+    fake = 1 << 20
+    common = dict(q=fake, k=fake, v=fake, kq=fake, kscale=fake, seq_lens=fake, out=fake, lse=fake, ws=fake,
+                  ws_bytes=1 << 40)
+    assert _decode(**common, max_seq_len=big, cap=big) == ffd.FFD_ERR_UNSUPPORTED
+    assert "2^30" in ffd.ffd_last_error()
+    assert ffd.ffd_decode_workspace_bytes(1, 32, 128, big, 64, 1) == 0
+    assert ffd.ffd_decode_multi_workspace_bytes(1, 2, 32, 128, big, 64, 1) == 0
+    assert ffd.ffd_decode_workspace_bytes(1, 32, 128, 2 ** 30, 64, 1) > 0
+    L = ffd.lib()
+    assert L.ffd_quantize_kv(fake, fake, fake, fake, fake, 1, 8, 128, 128, big, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert L.ffd_quantize_kv(fake, fake, fake, fake, fake, 1, 8, big, 128, 16, None) == ffd.FFD_ERR_UNSUPPORTED
+    assert L.ffd_quantize_kv_paged(fake, fake, fake, fake, 2 ** 25, 4, fake, fake, 1, 8, 128, 16,
+                                   None) == ffd.FFD_ERR_UNSUPPORTED
+    assert L.ffd_combine(fake, big, 1, 32, 128, 64, 32, fake, 1 << 40, fake, 0, fake, None) == ffd.FFD_ERR_UNSUPPORTED

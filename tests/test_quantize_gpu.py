@@ -72,3 +72,36 @@ def test_append_equals_build():
     torch.cuda.synchronize()
     assert torch.equal(kq_a, kq_b)
     assert torch.equal(ks_a.view(torch.int32), ks_b.view(torch.int32))
+
+
+def test_positions_near_int_max_touch_nothing():
+    """Positions are device values and are not validated: a range that starts
+    near INT_MAX (past the cache) or is empty leaves every byte as it was, in
+    both key storages; a range overlapping the cache quantises only its part."""
+    say("quantize: pos_begin near INT_MAX")
+    B, Hkv, d, cap = 2, 2, 128, 256
+    inp = make_random_inputs(B, Hkv, Hkv, d, (cap, cap), seed=71, block_size=64, hot_frac=0.0)
+    k = dev_bf16(inp["k"])
+    begin = torch.tensor([2 ** 31 - 3, 200], dtype=torch.int32, device="cuda")
+    end = torch.tensor([cap, 100], dtype=torch.int32, device="cuda")   # both empty
+    kq = torch.full((B, Hkv, cap, d // 2), 0xAB, dtype=torch.uint8, device="cuda")
+    ks = torch.full((B, Hkv, cap), -1.0, dtype=torch.float32, device="cuda")
+    ffd.ffd_quantize_kv(k, kq, ks, begin, end, cap)
+    k2 = torch.full((B, Hkv, cap, d // 4), 0xCD, dtype=torch.uint8, device="cuda")
+    k2s = torch.full((B, Hkv, cap), -2.0, dtype=torch.float32, device="cuda")
+    kr = torch.full((B, Hkv, cap, d), 7, dtype=torch.int8, device="cuda")
+    krs = torch.full((B, Hkv, cap), -3.0, dtype=torch.float32, device="cuda")
+    ffd.ffd_quantize_kv_thumb(k, k2, k2s, kr, krs, begin, end, cap)
+    torch.cuda.synchronize()
+    assert (kq == 0xAB).all() and (ks == -1.0).all()
+    assert (k2 == 0xCD).all() and (k2s == -2.0).all() and (kr == 7).all() and (krs == -3.0).all()
+    # a range that starts inside the cache and ends past it: only [begin, cap) is written
+    begin = torch.tensor([250, 0], dtype=torch.int32, device="cuda")
+    end = torch.tensor([2 ** 31 - 1, 0], dtype=torch.int32, device="cuda")
+    ffd.ffd_quantize_kv(k, kq, ks, begin, end, cap)
+    torch.cuda.synchronize()
+    rq, rs = O.quantize_cache(inp["k"], np.array([cap, 0]))
+    got_q, got_s = kq.cpu().numpy(), ks.cpu().numpy()
+    np.testing.assert_array_equal(got_q[0, :, 250:], rq[0, :, 250:cap])
+    np.testing.assert_array_equal(got_s[0, :, 250:], rs[0, :, 250:cap])
+    assert (got_q[0, :, :250] == 0xAB).all() and (got_q[1] == 0xAB).all()
