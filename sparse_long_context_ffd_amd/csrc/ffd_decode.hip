@@ -668,7 +668,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int qr = tid / QC, qk = tid % QC;
   u32x4_t qw = u32x4_t{0u, 0u, 0u, 0u};
   if (qr < R && qr / G < p.Q) qw = *reinterpret_cast<const u32x4_t*>(p.q + row_index<G>(p, b, j, qr) * D + qk * 8);
-  const int sl = p.seq_lens[b];
+  const int sl = max(p.seq_lens[b], 0);   // a device value: negative means empty (and must not wrap below)
   // the last query token sees the whole sequence: every load is bounded by it
   const int L = row_len<G>(p, sl, G * (p.Q - 1));
   const int NB = (L + kBlockSize - 1) / kBlockSize;

@@ -133,3 +133,29 @@ def test_workload(name, Q, full):
             assert_mask_equal(mask[b, i, h], r_mask[b, i, h], f"{name} mask {(b, i, h)}")
             assert_close(out[b, i, h], r_out[b, i, h], f"{name} out {(b, i, h)}")
             assert_close(lse[b, i, h], r_lse[b, i, h], f"{name} lse {(b, i, h)}")
+
+
+def test_negative_lengths_are_empty():
+    """seq_lens are device values and are not validated: any negative length,
+    INT_MIN included, is an empty sequence for every query token (out 0, LSE
+    -inf, zero mask), in both the several-token and the single-token call;
+    the other sequences of the batch are unaffected."""
+    B, Q, Hq, Hkv, d = 3, 3, 8, 2, 128
+    say("multi: negative lengths")
+    inp = make_random_inputs(B, Hq, Hkv, d, (700, 700, 700), seed=61, block_size=64, hot_frac=0.1)
+    qm = multi_query(inp, Q, seed=62)
+    dv = to_device(inp)
+    seq = torch.tensor([-2 ** 31, -5, 700], dtype=torch.int32, device="cuda")
+    kq, ks = ffd.quantize_kv(dv["k"], torch.tensor([700, 700, 700], dtype=torch.int32, device="cuda"))
+    kw = dict(max_seq_len=inp["cap"], delta=1.0, sink=1, local=2, split_blocks=4, sm_scale=sm_scale_for(d))
+    out, lse, mask = ffd.decode_multi(dev_bf16(qm), dv["k"], dv["v"], kq, ks, seq, out_dtype=torch.float32, **kw)
+    out1, lse1, mask1 = ffd.decode(dv["q"], dv["k"], dv["v"], kq, ks, seq, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    for o, l, m in ((out[:2], lse[:2], mask[:2]), (out1[:2], lse1[:2], mask1[:2])):
+        assert (o == 0).all() and torch.isneginf(l).all() and (m == 0).all()
+    r_out, r_lse, r_mask = O.decode_multi(qm, inp["k"], inp["v"], np.array([0, 0, 700]), block_size=64,
+                                          max_seq_len=inp["cap"], delta=1.0, sink=1, local=2, split_blocks=4,
+                                          sm_scale=np.float32(sm_scale_for(d)))
+    assert_mask_equal(mask.cpu().numpy(), r_mask, "mask")
+    assert_close(out.cpu().numpy().astype(np.float64), r_out, "out")
+    assert_close(lse.cpu().numpy().astype(np.float64), r_lse, "lse")
