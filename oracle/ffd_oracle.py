@@ -34,8 +34,10 @@ choice of this library, applied identically by the HIP path):
   global reduction. "sink_local": per query head, the maximum block score over
   the sink and local blocks, the estimate [TS] Methodology 2 (Pseudo-Max
   Approximation) and 3 (Pseudo-max Estimation) describe; the kept set then
-  does not depend on the split size. In both modes the sink blocks (first
-  ``sink``) and local blocks (last ``local``) are always kept.
+  does not depend on the split size. "max": per query head and split, the
+  larger of the two (so a low sink/local estimate cannot keep more of a split
+  than its own maximum would). In every mode the sink blocks (first ``sink``)
+  and local blocks (last ``local``) are always kept.
 * δ is in natural-log logit units ([TS] Methodology 2, "Adaptivity"), the
   comparison is ``>=`` ([TS] Methodology 2, "Mechanism"), and the logit is
   ``sm_scale * q.k``.
@@ -271,16 +273,17 @@ def block_scores(tok: np.ndarray, L: int, block_size: int) -> np.ndarray:
 # O5 + O6: split-local Top-δ with sink and local blocks   [TS] Methodology 2
 # --------------------------------------------------------------------------
 
-PSEUDO_MAX_MODES = ("split", "sink_local")
+PSEUDO_MAX_MODES = ("split", "sink_local", "max")
 
 
 def select_blocks(scores: np.ndarray, split_blocks: int, delta, sink: int, local: int,
                   pseudo_max: str = "split") -> np.ndarray:
     """Keep block j iff score_j >= m~ - δ, or j is one of the first ``sink`` or
     last ``local`` blocks. m~ is the maximum block score in j's split (blocks
-    [s*S, s*S+S)) for ``pseudo_max="split"``, or the maximum over the sink and
-    local blocks for ``pseudo_max="sink_local"``. The subtraction and
-    comparison run in the dtype of ``scores`` (fp32 for the quantised scan)."""
+    [s*S, s*S+S)) for ``pseudo_max="split"``, the maximum over the sink and
+    local blocks for ``pseudo_max="sink_local"``, and the larger of the two
+    for ``pseudo_max="max"``. The subtraction and comparison run in the dtype
+    of ``scores`` (fp32 for the quantised scan)."""
     if pseudo_max not in PSEUDO_MAX_MODES:
         raise ValueError(f"pseudo_max must be one of {PSEUDO_MAX_MODES}")
     dt = scores.dtype.type
@@ -291,18 +294,22 @@ def select_blocks(scores: np.ndarray, split_blocks: int, delta, sink: int, local
     forced[:min(sink, nb)] = True
     if local > 0:
         forced[max(0, nb - local):] = True
-    if pseudo_max == "split":
+    m_sl = None
+    if pseudo_max != "split":
+        if sink + local < 1:
+            raise ValueError("the sink/local pseudo-max needs sink + local >= 1")
+        m_sl = dt(np.max(scores[forced]))
+    if pseudo_max == "sink_local":
+        thr = dt(m_sl - d)
+        keep = scores >= thr
+    else:
         for s0 in range(0, nb, split_blocks):
             seg = scores[s0:s0 + split_blocks]
             m_tilde = dt(np.max(seg))
+            if pseudo_max == "max":
+                m_tilde = max(m_tilde, m_sl)
             thr = dt(m_tilde - d)
             keep[s0:s0 + split_blocks] = seg >= thr
-    else:
-        if sink + local < 1:
-            raise ValueError("the sink/local pseudo-max needs sink + local >= 1")
-        m_tilde = dt(np.max(scores[forced]))
-        thr = dt(m_tilde - d)
-        keep = scores >= thr
     return keep | forced
 
 

@@ -1,6 +1,8 @@
-"""The sink/local pseudo-max mode of the oracle: a hand-worked 3-block
-example, independence from the split size, monotonicity in δ, and the
-brute-force token rule with m~ taken over the sink and local tokens."""
+"""The sink/local pseudo-max modes of the oracle: a hand-worked 3-block
+example, independence from the split size, monotonicity in δ, the
+brute-force token rule with m~ taken over the sink and local tokens, and the
+"max" mode (the larger of the split max and the sink/local estimate) keeping
+exactly the blocks both other modes keep."""
 
 import json
 import math
@@ -30,7 +32,7 @@ def test_block_scores(hand):
     assert O.block_scores(tok, 6, 2).tolist() == hand["block_scores"]
 
 
-@pytest.mark.parametrize("idx", range(7))
+@pytest.mark.parametrize("idx", range(10))
 def test_cases(hand, idx):
     c = hand["cases"][idx]
     inp = hand["inputs"]
@@ -128,3 +130,34 @@ def test_splits_may_keep_nothing_and_attention_stays_exact():
         p = np.exp(z - z.max())
         np.testing.assert_allclose(out[0, h], p @ vv / p.sum(), atol=1e-12)
         assert abs(lse[0, h] - (z.max() + math.log(p.sum()))) < 1e-12
+
+
+@SET
+@given(seed=st.integers(0, 10_000), delta=st.floats(0, 4), sink=st.integers(0, 2), local=st.integers(0, 3),
+       S=st.integers(1, 6))
+def test_max_mode_keeps_what_both_modes_keep(seed, delta, sink, local, S):
+    """fl32(m - δ) is monotone in m, so the threshold of max(m_split, m_sl) is
+    the larger of the two thresholds and a block passes it iff it passes both:
+    the kept set of "max" is the intersection of the other two (forced blocks
+    in all three)."""
+    if sink + local == 0:
+        local = 1
+    inp, L = _case(seed)
+    kw = dict(max_seq_len=L, block_size=8, delta=np.float32(delta), sink=sink, local=local, split_blocks=S,
+              sm_scale=np.float32(0.25), mask_only=True)
+    masks = {pm: O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], pseudo_max=pm, **kw)[2]
+             for pm in ("split", "sink_local", "max")}
+    np.testing.assert_array_equal(masks["max"], masks["split"] & masks["sink_local"])
+
+
+def test_max_mode_multi_query():
+    """The same identity per query token with several tokens per sequence."""
+    inp, L = _case(77, L=300)
+    from ffd_inputs import multi_query
+    qm = multi_query(inp, 3, seed=78)
+    kw = dict(max_seq_len=L, block_size=8, delta=0.7, sink=1, local=2, split_blocks=4, sm_scale=np.float32(0.25),
+              mask_only=True)
+    masks = {pm: O.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], pseudo_max=pm, **kw)[2]
+             for pm in ("split", "sink_local", "max")}
+    np.testing.assert_array_equal(masks["max"], masks["split"] & masks["sink_local"])
+    assert (masks["max"] != masks["split"]).any() or (masks["max"] != masks["sink_local"]).any()
