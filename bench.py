@@ -165,8 +165,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--delta", type=float, default=None, help="default: the workload's first delta")
-    ap.add_argument("--pseudo-max", default="split", choices=["split", "sink_local"],
-                    help="split-local max (default) or the sink/local estimate")
+    ap.add_argument("--pseudo-max", default="split", choices=["split", "sink_local", "max"],
+                    help="split-local max (default), the sink/local estimate, or the larger of the two")
     ap.add_argument("--storage", default="int4", choices=["int4", "thumb"],
                     help="int4 sketch + bf16 K (default) or 2-bit thumbnails + int8 residuals")
     ap.add_argument("--queries", type=int, default=1,

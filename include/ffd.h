@@ -47,9 +47,12 @@ typedef enum { FFD_OUT_BF16 = 0, FFD_OUT_F32 = 1 } ffd_out_dtype;
 /* How the pseudo-max m~ of the Top-δ rule is estimated ([TS] Methodology 2). */
 typedef enum {
   FFD_PSEUDO_MAX_SPLIT = 0,      /* max block score within the block's split (one workgroup) */
-  FFD_PSEUDO_MAX_SINK_LOCAL = 1  /* max block score over the sink and local blocks ([TS]
+  FFD_PSEUDO_MAX_SINK_LOCAL = 1, /* max block score over the sink and local blocks ([TS]
                                     Methodology 2 "Pseudo-Max Approximation", 3 "Pseudo-max
                                     Estimation"); the kept set does not depend on split_blocks */
+  FFD_PSEUDO_MAX_BOTH = 2        /* per split, the larger of the two above: a block is kept iff
+                                    both other modes keep it (a low sink/local estimate cannot
+                                    widen a split's kept set beyond its own maximum) */
 } ffd_pseudo_max;
 
 /* Version of this ABI (FFD_ABI_VERSION). */
@@ -157,8 +160,9 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *   3. Top-δ ([TS] Methodology 2, "Mechanism"): block j is kept iff
  *      score_j >= fl32(m~ - delta), or j < sink_blocks, or j >= NB -
  *      local_blocks. m~ is the max block score in j's split
- *      (FFD_PSEUDO_MAX_SPLIT) or over the sink and local blocks
- *      (FFD_PSEUDO_MAX_SINK_LOCAL). δ is in natural-log logit units ([TS]
+ *      (FFD_PSEUDO_MAX_SPLIT), over the sink and local blocks
+ *      (FFD_PSEUDO_MAX_SINK_LOCAL), or the larger of the two
+ *      (FFD_PSEUDO_MAX_BOTH). δ is in natural-log logit units ([TS]
  *      Methodology 2, "Adaptivity").
  *   4. Refinement ([TS] Methodology 3, "Fine-Grained Refinement"): exact
  *      softmax attention (logit = sm_scale * q.k on the bf16 values, fp32
@@ -174,8 +178,9 @@ size_t ffd_decode_workspace_bytes(int B, int Hq, int d, int max_seq_len, int blo
  *   max_seq_len host; bounds every L and sizes the grid and the mask
  *   delta      >= 0 (fp32), +INFINITY allowed
  *   sink_blocks, local_blocks >= 0
- *   pseudo_max FFD_PSEUDO_MAX_SPLIT or FFD_PSEUDO_MAX_SINK_LOCAL (the latter
- *              needs 1 <= sink_blocks + local_blocks <= 64)
+ *   pseudo_max FFD_PSEUDO_MAX_SPLIT, FFD_PSEUDO_MAX_SINK_LOCAL or
+ *              FFD_PSEUDO_MAX_BOTH (the last two need
+ *              1 <= sink_blocks + local_blocks <= 64)
  *   split_blocks in [1, 64]; with FFD_PSEUDO_MAX_SPLIT part of the semantics
  *              (the kept set depends on it); otherwise only a work partition
  *   sm_scale   > 0 and finite (commonly fl32(1/sqrt(d)))
@@ -223,7 +228,7 @@ ffd_status ffd_decode(const void* q, const void* k, const void* v,
  *   workspace  >= ffd_decode_multi_workspace_bytes(B, Q, Hq, d, max_seq_len,
  *              block_size, split_blocks) bytes, 256-byte aligned
  * Everything else as ffd_decode. Supported: Q >= 1 with (Hq / Hkv) * Q <= 16;
- * with FFD_PSEUDO_MAX_SINK_LOCAL, sink_blocks + local_blocks +
+ * with FFD_PSEUDO_MAX_SINK_LOCAL or FFD_PSEUDO_MAX_BOTH, sink_blocks + local_blocks +
  * ceil((Q - 1) / 64) <= 64. FFD_ERR_UNSUPPORTED otherwise. Q == 1 is ffd_decode.
  */
 ffd_status ffd_decode_multi(const void* q, const void* k, const void* v,

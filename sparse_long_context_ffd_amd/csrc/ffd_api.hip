@@ -181,9 +181,10 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   if (!(sm_scale > 0.f) || isinf(sm_scale))
     return fail(FFD_ERR_INVALID_ARG, "%s: sm_scale must be positive and finite (got %g)", fn, (double)sm_scale);
   if (block_size <= 0) return fail(FFD_ERR_INVALID_ARG, "%s: block_size must be positive (got %d)", fn, block_size);
-  if (pseudo_max != FFD_PSEUDO_MAX_SPLIT && pseudo_max != FFD_PSEUDO_MAX_SINK_LOCAL)
+  if (pseudo_max != FFD_PSEUDO_MAX_SPLIT && pseudo_max != FFD_PSEUDO_MAX_SINK_LOCAL &&
+      pseudo_max != FFD_PSEUDO_MAX_BOTH)
     return fail(FFD_ERR_INVALID_ARG, "%s: unknown pseudo_max mode %d", fn, pseudo_max);
-  if (pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL && (long)sink_blocks + local_blocks < 1)
+  if (pseudo_max != FFD_PSEUDO_MAX_SPLIT && (long)sink_blocks + local_blocks < 1)
     return fail(FFD_ERR_INVALID_ARG, "%s: the sink/local pseudo-max needs sink_blocks + local_blocks >= 1", fn);
   G = Hq / Hkv;
   if (d != 64 && d != 128) return fail(FFD_ERR_UNSUPPORTED, "%s: d=%d not supported (64, 128)", fn, d);
@@ -195,7 +196,7 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   if (split_blocks > ffd::kMaxSplit)
     return fail(FFD_ERR_UNSUPPORTED, "%s: split_blocks=%d not supported (<= %d)", fn, split_blocks, ffd::kMaxSplit);
   // the query tokens' local windows together span local + ceil((Q - 1) / 64) + 1 blocks at most
-  if (pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL &&
+  if (pseudo_max != FFD_PSEUDO_MAX_SPLIT &&
       (long)sink_blocks + local_blocks + (Q > 1 ? (Q - 1 + ffd::kBlockSize - 1) / ffd::kBlockSize : 0) >
           ffd::kMaxPseudoMax)
     return fail(FFD_ERR_UNSUPPORTED, "%s: sink_blocks + local_blocks = %ld exceeds %d with the sink/local pseudo-max",
@@ -251,7 +252,8 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.split_blocks = split_blocks;
   p.sink = sink_blocks;
   p.local = local_blocks;
-  p.pm_sink_local = pseudo_max == FFD_PSEUDO_MAX_SINK_LOCAL;
+  p.pm_sink_local = pseudo_max != FFD_PSEUDO_MAX_SPLIT;
+  p.pm_with_split = pseudo_max == FFD_PSEUDO_MAX_BOTH;
   p.delta = delta;
   p.sm_scale = sm_scale;
   return FFD_OK;

@@ -282,10 +282,11 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
 // Row r (query token r / G, head r % G) sees NB_r blocks; a block it cannot see
 // is never kept for it, and its sink/local blocks are those of its own range.
 // Wave w takes rows w, w + 4, ...; lane = block of the split. Per row: the
-// split max m~ (the seed of its softmax, and the pseudo-max in split mode) or
+// split max m~ (the seed of its softmax, and the pseudo-max in split mode),
 // the sink/local estimate (max over the row's own sink and local blocks, the
-// extra ones scanned outside the split first), the threshold fl32(pm - δ),
-// the forced blocks; the row's keep bits go to LDS per wave.
+// extra ones scanned outside the split first), or the larger of the two; the
+// threshold fl32(pm - δ), the forced blocks; the row's keep bits go to LDS
+// per wave.
 template <int D, int G, int QT>
 __device__ __forceinline__ void select_rows(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int j0, int nblk,
                                             int nx, int sl, int lane, int w) {
@@ -311,6 +312,7 @@ __device__ __forceinline__ void select_rows(const DecodeParams& p, DecodeSmem<D,
     const bool forced = jb < p.sink || jb >= NBr - p.local;
     const float mt = wave_max_f(s);
     if (!p.pm_sink_local) pm = mt;
+    else if (p.pm_with_split) pm = fmaxf(pm, mt);
     const float thr = pm - p.delta;
     if (vis && (s >= thr || forced)) hm |= 1u << r;
     if (lane == 0) sm.seed[r] = mt;

@@ -54,6 +54,7 @@ struct DecodeParams {
   int split_blocks;
   int sink, local;
   int pm_sink_local;       // 1: pseudo-max over the sink/local blocks; 0: split max
+  int pm_with_split;       // with pm_sink_local: the larger of that estimate and the split max
   float delta, sm_scale;
 };
 

@@ -34,7 +34,7 @@ FFD_ERR_WORKSPACE = 3
 FFD_ERR_HIP = 4
 FFD_OUT_BF16 = 0
 FFD_OUT_F32 = 1
-PSEUDO_MAX = {"split": 0, "sink_local": 1}
+PSEUDO_MAX = {"split": 0, "sink_local": 1, "max": 2}
 
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_quantize_kv_paged",
                     "ffd_quantize_kv_thumb", "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged",

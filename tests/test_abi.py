@@ -71,8 +71,10 @@ def _decode(**kw):
     (dict(block_size=32), ffd.FFD_ERR_UNSUPPORTED, "block_size"),
     (dict(Hq=12, Hkv=4), ffd.FFD_ERR_UNSUPPORTED, "group size"),
     (dict(split=65), ffd.FFD_ERR_UNSUPPORTED, "split_blocks"),
-    (dict(pm=2), ffd.FFD_ERR_INVALID_ARG, "pseudo_max"),
+    (dict(pm=3), ffd.FFD_ERR_INVALID_ARG, "pseudo_max"),
     (dict(pm=1, sink=0, local=0), ffd.FFD_ERR_INVALID_ARG, "sink/local"),
+    (dict(pm=2, sink=0, local=0), ffd.FFD_ERR_INVALID_ARG, "sink/local"),
+    (dict(pm=2, sink=40, local=30), ffd.FFD_ERR_UNSUPPORTED, "exceeds"),
     (dict(pm=1, sink=40, local=30), ffd.FFD_ERR_UNSUPPORTED, "exceeds"),
     (dict(), ffd.FFD_ERR_INVALID_ARG, "null"),
 ])

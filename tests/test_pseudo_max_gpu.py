@@ -1,6 +1,7 @@
-"""GPU parity for the sink/local pseudo-max: mask bit-exact and out/LSE within
-the bar against the oracle, including splits that keep no block at all, and
-the 128K x4 workload at full size."""
+"""GPU parity for the sink/local pseudo-max modes ("sink_local", and "max":
+the larger of the split max and the sink/local estimate): mask bit-exact and
+out/LSE within the bar against the oracle, including splits that keep no
+block at all, and the 128K x4 workload at full size."""
 
 import math
 
@@ -24,20 +25,35 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("pm", ["sink_local", "max"])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_small_cases(case):
+def test_small_cases(case, pm):
     B, Hq, Hkv, d, lens, delta, sink, local, S = CASES[case]
-    say(f"sink_local case {case}: B={B} Hq={Hq} Hkv={Hkv} d={d} lens={lens} delta={delta} S={S}")
+    say(f"{pm} case {case}: B={B} Hq={Hq} Hkv={Hkv} d={d} lens={lens} delta={delta} S={S}")
     inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=500 + case, block_size=64, hot_frac=0.1)
     sm = sm_scale_for(d)
     out, lse, mask = run_gpu(to_device(inp), max_seq_len=inp["cap"], delta=delta, sink=sink, local=local,
-                             split_blocks=S, sm_scale=sm, pseudo_max="sink_local")
+                             split_blocks=S, sm_scale=sm, pseudo_max=pm)
     r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], max_seq_len=inp["cap"],
                                     block_size=64, delta=delta, sink=sink, local=local, split_blocks=S,
-                                    sm_scale=np.float32(sm), pseudo_max="sink_local")
+                                    sm_scale=np.float32(sm), pseudo_max=pm)
     assert_mask_equal(mask, r_mask, "mask")
     assert_close(out, r_out, "out")
     assert_close(lse, r_lse, "lse")
+
+
+def test_max_mode_is_the_intersection_on_the_gpu():
+    """On the GPU too, the "max" mode keeps exactly the blocks both the split
+    and the sink/local modes keep (same cache, same query)."""
+    say("max mode = split AND sink_local (GPU)")
+    inp = make_random_inputs(2, 16, 4, 128, (6000, 2500), seed=520, block_size=64, hot_frac=0.1)
+    dv = to_device(inp)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    kw = dict(max_seq_len=inp["cap"], delta=0.75, sink=1, local=3, split_blocks=8, sm_scale=sm_scale_for(128),
+              kq=kq, kscale=ks)
+    m = {pm: run_gpu(dv, pseudo_max=pm, **kw)[2] for pm in ("split", "sink_local", "max")}
+    np.testing.assert_array_equal(m["max"], m["split"] & m["sink_local"])
+    assert (m["max"] != m["split"]).any() and (m["max"] != m["sink_local"]).any()
 
 
 def test_whole_splits_dropped():
