@@ -249,8 +249,8 @@ def main() -> int:
         torch.cuda.synchronize()
 
     Q = args.queries
-    if Q > 1 and (args.paged or args.storage == "thumb"):
-        print("bench.py: --queries is only implemented for the contiguous int4 storage", file=sys.stderr)
+    if Q > 1 and args.storage == "thumb":
+        print("bench.py: --queries is only implemented for the int4 storage", file=sys.stderr)
         return 2
     qm_bits = multi_query(inp, Q, seed=w.seed + 1000) if Q > 1 else None
     qm = bf16(qm_bits) if Q > 1 else None
@@ -293,6 +293,15 @@ def main() -> int:
     def step(dl, ev=None):
         if ev is not None:
             ev[0].record()
+        if Q > 1 and args.paged:
+            ffd.ffd_decode_paged_multi(qm, kp, vp, None if math.isinf(dl) else kqp, None if math.isinf(dl) else ksp,
+                                       table, seq, delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale,
+                                       out=out, lse=lse, kept_mask=mask, workspace=ws, pseudo_max=args.pseudo_max,
+                                       **kw)
+            if ev is not None:
+                ev[1].record()
+                ev[2].record()
+            return
         if Q > 1:
             ffd.ffd_decode_multi(qm, k, v, None if math.isinf(dl) else kq, None if math.isinf(dl) else ks, seq,
                                  delta=dl, sink=w.sink, local=w.local, sm_scale=sm_scale, out=out, lse=lse,
@@ -402,7 +411,9 @@ def main() -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("fused_decode_kernel + combine_kernel (ffd_decode_paged)" if args.paged else
+            "kernel": (f"fused_decode_kernel<{Q} query tokens> + combine_kernel (ffd_decode_paged_multi)"
+                       if args.paged and Q > 1 else
+                       "fused_decode_kernel + combine_kernel (ffd_decode_paged)" if args.paged else
                        f"fused_decode_kernel<{Q} query tokens> + combine_kernel (ffd_decode_multi)" if Q > 1
                        else "fused_decode_kernel<thumb> + combine_kernel (ffd_decode_thumb)" if args.storage == "thumb"
                        else "fused_decode_kernel (scan, select, attend; issued by ffd_decode_partials)"),

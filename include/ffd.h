@@ -263,6 +263,23 @@ ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pa
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ffd_decode_paged_multi -- ffd_decode_multi on a paged KV cache: Q query
+ * tokens per sequence (q [B, Q, Hq, d], outputs [B, Q, Hq, ...]) with the
+ * semantics of ffd_decode_multi, over pages laid out and addressed as for
+ * ffd_decode_paged. Workspace: ffd_decode_multi_workspace_bytes. A paged
+ * cache holding the same rows gives outputs bit-identical to
+ * ffd_decode_multi. Supported as ffd_decode_multi.
+ */
+ffd_status ffd_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
+                                  const uint8_t* kq_pages, const float* kscale_pages,
+                                  const int32_t* block_table, int table_stride, int num_pages,
+                                  const int32_t* seq_lens, int max_seq_len, int B, int Q, int Hq, int Hkv,
+                                  int d, int block_size, float delta, int sink_blocks, int local_blocks,
+                                  int pseudo_max, int split_blocks, float sm_scale,
+                                  void* out, int out_dtype, float* lse, uint8_t* kept_mask,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ffd_decode_thumb -- ffd_decode over the thumbnail + residual key storage of
  * ffd_quantize_kv_thumb (no bf16 K is read). The scan uses the thumbnail:
  * dot = sum qc_i (2u_i - 3) (exact integer), score fl32(float(dot) *

@@ -24,6 +24,7 @@ from .ffd import (  # noqa: F401
     ffd_decode_multi,
     ffd_decode_multi_workspace_bytes,
     ffd_decode_paged,
+    ffd_decode_paged_multi,
     ffd_decode_partials,
     ffd_decode_thumb,
     ffd_decode_workspace_bytes,

@@ -327,13 +327,18 @@ ffd_status ffd_decode_multi(const void* q, const void* k, const void* v, const u
   return launch(fn, p, d, G, dense, ffd::Stage::kBoth, stream);
 }
 
-ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pages, const uint8_t* kq_pages,
-                            const float* kscale_pages, const int32_t* block_table, int table_stride, int num_pages,
-                            const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d,
-                            int block_size, float delta, int sink_blocks, int local_blocks, int pseudo_max,
-                            int split_blocks, float sm_scale, void* out, int out_dtype, float* lse,
-                            uint8_t* kept_mask, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "ffd_decode_paged";
+}  // extern "C"
+
+namespace {
+
+// ffd_decode_paged and ffd_decode_paged_multi: the block-table path for Q
+// query tokens per sequence (Q = 1: single-token decode).
+ffd_status decode_paged(const char* fn, const void* q, const void* k_pages, const void* v_pages,
+                        const uint8_t* kq_pages, const float* kscale_pages, const int32_t* block_table,
+                        int table_stride, int num_pages, const int32_t* seq_lens, int max_seq_len, int B, int Q,
+                        int Hq, int Hkv, int d, int block_size, float delta, int sink_blocks, int local_blocks,
+                        int pseudo_max, int split_blocks, float sm_scale, void* out, int out_dtype, float* lse,
+                        uint8_t* kept_mask, void* workspace, size_t workspace_bytes, void* stream) {
   if (max_seq_len > 0 && B > 0 && !block_table) return fail(FFD_ERR_INVALID_ARG, "%s: null block_table", fn);
   ffd::DecodeParams p;
   int G;
@@ -341,7 +346,7 @@ ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pa
   ffd_status st = check_out_dtype(fn, out_dtype);
   if (st != FFD_OK) return st;
   const int32_t* table = (max_seq_len > 0 && B > 0) ? block_table : nullptr;
-  st = prepare_decode(fn, q, k_pages, v_pages, kq_pages, kscale_pages, seq_lens, max_seq_len, B, 1, Hq, Hkv, d,
+  st = prepare_decode(fn, q, k_pages, v_pages, kq_pages, kscale_pages, seq_lens, max_seq_len, B, Q, Hq, Hkv, d,
                       max_seq_len, block_size, delta, sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale,
                       kept_mask, workspace, workspace_bytes, table, table_stride, num_pages, p, G, dense);
   if (st != FFD_OK) return st;
@@ -351,6 +356,35 @@ ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pa
   p.lse = lse;
   p.out_f32 = out_dtype == FFD_OUT_F32;
   return launch(fn, p, d, G, dense, ffd::Stage::kBoth, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pages, const uint8_t* kq_pages,
+                            const float* kscale_pages, const int32_t* block_table, int table_stride, int num_pages,
+                            const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d,
+                            int block_size, float delta, int sink_blocks, int local_blocks, int pseudo_max,
+                            int split_blocks, float sm_scale, void* out, int out_dtype, float* lse,
+                            uint8_t* kept_mask, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_paged("ffd_decode_paged", q, k_pages, v_pages, kq_pages, kscale_pages, block_table, table_stride,
+                      num_pages, seq_lens, max_seq_len, B, 1, Hq, Hkv, d, block_size, delta, sink_blocks,
+                      local_blocks, pseudo_max, split_blocks, sm_scale, out, out_dtype, lse, kept_mask, workspace,
+                      workspace_bytes, stream);
+}
+
+ffd_status ffd_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages, const uint8_t* kq_pages,
+                                  const float* kscale_pages, const int32_t* block_table, int table_stride,
+                                  int num_pages, const int32_t* seq_lens, int max_seq_len, int B, int Q, int Hq,
+                                  int Hkv, int d, int block_size, float delta, int sink_blocks, int local_blocks,
+                                  int pseudo_max, int split_blocks, float sm_scale, void* out, int out_dtype,
+                                  float* lse, uint8_t* kept_mask, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return decode_paged("ffd_decode_paged_multi", q, k_pages, v_pages, kq_pages, kscale_pages, block_table,
+                      table_stride, num_pages, seq_lens, max_seq_len, B, Q, Hq, Hkv, d, block_size, delta,
+                      sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, out, out_dtype, lse, kept_mask,
+                      workspace, workspace_bytes, stream);
 }
 
 ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2scale, const int8_t* kr,

@@ -10,7 +10,7 @@ the int4 sketch ``ffd_quantize_kv`` / ``ffd_decode`` and its halves
 ``ffd_decode_partials`` / ``ffd_combine``, the thumbnail storage
 ``ffd_quantize_kv_thumb`` / ``ffd_decode_thumb``, the paged cache
 ``ffd_quantize_kv_paged`` / ``ffd_decode_paged``, several query tokens
-``ffd_decode_multi``, the workspace sizes, ``ffd_last_error`` and
+``ffd_decode_multi`` / ``ffd_decode_paged_multi``, the workspace sizes, ``ffd_last_error`` and
 ``ffd_abi_version``) and take preallocated tensors. ``quantize_kv``,
 ``quantize_kv_thumb``, ``decode`` and ``decode_multi`` are conveniences that
 allocate the outputs and the workspace with torch and then call them.
@@ -39,7 +39,7 @@ PSEUDO_MAX = {"split": 0, "sink_local": 1, "max": 2}
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_quantize_kv_paged",
                     "ffd_quantize_kv_thumb", "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged",
                     "ffd_decode_thumb", "ffd_decode_partials", "ffd_combine", "ffd_decode_multi",
-                    "ffd_decode_multi_workspace_bytes")
+                    "ffd_decode_multi_workspace_bytes", "ffd_decode_paged_multi")
 
 
 class FFDError(RuntimeError):
@@ -99,6 +99,12 @@ def lib() -> ctypes.CDLL:
                                    _i, ctypes.c_float, _i, _i, _i, _i,        # block_size delta sink local pm split
                                    ctypes.c_float, _vp, _i, _vp, _vp,         # sm_scale out out_dtype lse mask
                                    _vp, ctypes.c_size_t, _vp]                 # workspace bytes stream
+    L.ffd_decode_paged_multi.restype = _i
+    L.ffd_decode_paged_multi.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i,  # q kp vp kqp ksp table stride pages
+                                         _vp, _i, _i, _i, _i, _i, _i,        # seq_lens max_seq_len B Q Hq Hkv d
+                                         _i, ctypes.c_float, _i, _i, _i, _i,  # block_size delta sink local pm split
+                                         ctypes.c_float, _vp, _i, _vp, _vp,   # sm_scale out out_dtype lse mask
+                                         _vp, ctypes.c_size_t, _vp]           # workspace bytes stream
     L.ffd_quantize_kv_thumb.restype = _i
     L.ffd_quantize_kv_thumb.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     L.ffd_decode_thumb.restype = _i
@@ -321,6 +327,44 @@ def ffd_decode_paged(q, k_pages, v_pages, kq_pages, kscale_pages, block_table, s
                                   Hkv, d, int(block_size), float(delta), int(sink), int(local), _pm(pseudo_max),
                                   int(split_blocks), float(sm_scale), _ptr(out), odt, _ptr(lse), _ptr(kept_mask),
                                   _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def ffd_decode_paged_multi(q, k_pages, v_pages, kq_pages, kscale_pages, block_table, seq_lens, *,
+                           max_seq_len: int, block_size: int, delta: float, sink: int, local: int,
+                           split_blocks: int, sm_scale: float, out: torch.Tensor, lse: torch.Tensor,
+                           kept_mask: Optional[torch.Tensor], workspace: Optional[torch.Tensor],
+                           pseudo_max: str = "split", stream=None) -> None:
+    """Q query tokens per sequence (``q`` ``[B, Q, Hq, d]``, as
+    :func:`ffd_decode_multi`) over a paged cache (as :func:`ffd_decode_paged`)
+    into preallocated ``out`` ``[B, Q, Hq, d]`` / ``lse`` ``[B, Q, Hq]`` /
+    ``kept_mask`` ``[B, Q, Hq, NB]``."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    B, Q, Hq, d = q.shape
+    P, Hkv, bs, _ = k_pages.shape
+    if bs != 64 or tuple(k_pages.shape) != (P, Hkv, 64, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k/v pages must be [num_pages, Hkv, 64, d]")
+    _need(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table needs one row per sequence")
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if kq_pages is not None:
+        _need(kq_pages, "kq_pages", torch.uint8, 4)
+        _need(kscale_pages, "kscale_pages", torch.float32, 3)
+    if kept_mask is not None:
+        _need(kept_mask, "kept_mask", torch.uint8, 4)
+        if tuple(kept_mask.shape) != (B, Q, Hq, -(-max_seq_len // block_size)):
+            raise ValueError("kept_mask shape")
+    if tuple(out.shape[:3]) != (B, Q, Hq) or tuple(lse.shape) != (B, Q, Hq):
+        raise ValueError("out/lse shapes")
+    odt = _check_outputs(out.view(B, Q * Hq, out.shape[-1]), lse.view(B, Q * Hq), B, Q * Hq, d)
+    _check(lib().ffd_decode_paged_multi(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(kq_pages), _ptr(kscale_pages),
+                                        _ptr(block_table), block_table.shape[1], P, _ptr(seq_lens), int(max_seq_len),
+                                        B, Q, Hq, Hkv, d, int(block_size), float(delta), int(sink), int(local),
+                                        _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out), odt,
+                                        _ptr(lse), _ptr(kept_mask), _ptr(workspace), _ws(workspace),
+                                        _stream(stream)))
 
 
 def ffd_quantize_kv_thumb(k, k2, k2scale, kr, krscale, pos_begin, pos_end, max_span: int, stream=None) -> None:

@@ -122,6 +122,34 @@ def test_paged_validation():
     assert st == ffd.FFD_ERR_INVALID_ARG and "block_table" in ffd.ffd_last_error()
 
 
+def test_paged_multi_validation():
+    """The multi-query block-table call checks its table and its query count
+    like the single-token one, before any launch."""
+    L = ffd.lib()
+    f = ctypes.c_float
+    fake = 1 << 20
+
+    def call(table, stride, num_pages, Q, Hq=8, Hkv=2, ws_bytes=1 << 30):
+        return L.ffd_decode_paged_multi(fake, fake, fake, fake, fake, table, stride, num_pages, fake, 256, 1, Q, Hq,
+                                        Hkv, 128, 64, f(2.0), 1, 1, 0, 32, f(0.1), fake, 0, fake, fake, fake,
+                                        ws_bytes, None)
+
+    assert call(None, 4, 10, 2) == ffd.FFD_ERR_INVALID_ARG and "block_table" in ffd.ffd_last_error()
+    assert call(fake, 3, 10, 2) == ffd.FFD_ERR_INVALID_ARG and "table_stride" in ffd.ffd_last_error()
+    assert call(fake, 4, 0, 2) == ffd.FFD_ERR_INVALID_ARG and "num_pages" in ffd.ffd_last_error()
+    assert call(fake, 4, 10, 0) == ffd.FFD_ERR_INVALID_ARG and "Q=0" in ffd.ffd_last_error()
+    assert call(fake, 4, 10, 5, Hq=4, Hkv=1) == ffd.FFD_ERR_UNSUPPORTED
+    assert "ffd_decode_paged_multi" in ffd.ffd_last_error()
+    one = ffd.ffd_decode_workspace_bytes(1, 8, 128, 256, 64, 32)
+    assert call(fake, 4, 10, 2, ws_bytes=one) == ffd.FFD_ERR_WORKSPACE
+
+
+def test_package_reexports_every_entry_point():
+    """Each C entry point has a wrapper of the same name at package level."""
+    for n in ffd.EXPORTED_SYMBOLS:
+        assert callable(getattr(ffd, n, None)), n
+
+
 def _decode_multi(**kw):
     args = dict(q=None, k=None, v=None, kq=None, kscale=None, seq_lens=None, max_seq_len=128, B=1, Q=2, Hq=4, Hkv=1,
                 d=128, cap=128, block_size=64, delta=6.0, sink=1, local=4, pm=0, split=32, sm_scale=0.088388,

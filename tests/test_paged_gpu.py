@@ -1,6 +1,6 @@
-"""Paged KV cache: ffd_quantize_kv_paged / ffd_decode_paged over a shuffled
-page pool give bit-identical results to the contiguous entry points on the
-same rows, and match the oracle."""
+"""Paged KV cache: ffd_quantize_kv_paged / ffd_decode_paged /
+ffd_decode_paged_multi over a shuffled page pool give bit-identical results
+to the contiguous entry points on the same rows, and match the oracle."""
 
 import numpy as np
 import pytest
@@ -161,3 +161,61 @@ def test_paged_full_size_bit_identical(pm):
         res.append((out, lse, mask))
     for a, b_ in zip(res[0], res[1]):
         assert torch.equal(a, b_)
+
+
+@pytest.mark.parametrize("B,Q,Hq,Hkv,d,lens,delta,pm,S", [
+    (2, 3, 8, 2, 128, (2500, 700), 1.0, "split", 4),
+    (3, 4, 4, 1, 64, (1500, 3, 900), 0.5, "sink_local", 8),
+    (1, 2, 32, 8, 128, (8000,), 2.0, "max", 32),
+])
+def test_paged_multi_equals_contiguous_multi(B, Q, Hq, Hkv, d, lens, delta, pm, S):
+    """ffd_decode_paged_multi over shuffled pages is bit-identical to
+    ffd_decode_multi on the same rows (several query tokens per sequence,
+    padding rows, a token that sees nothing) and matches the oracle."""
+    from ffd_inputs import multi_query
+    from tests.gpu_util import dev_bf16
+    say(f"paged multi B={B} Q={Q} Hq={Hq} Hkv={Hkv} d={d} lens={lens} delta={delta} {pm} S={S}")
+    inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=950 + B, block_size=64, hot_frac=0.1)
+    qm = multi_query(inp, Q, seed=960 + B)
+    dv = to_device(inp)
+    cap = inp["cap"]
+    nbs = [-(-L // 64) for L in lens]
+    num_pages = sum(nbs) + 3
+    perm = np.random.default_rng(5).permutation(num_pages)
+    stride = cap // 64 + 1
+    table_np = np.full((B, stride), 10 ** 6, dtype=np.int32)   # unused entries out of range (clamped)
+    used = 0
+    for b in range(B):
+        table_np[b, :nbs[b]] = perm[used:used + nbs[b]]
+        used += nbs[b]
+    table = torch.from_numpy(table_np).cuda()
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    pools = [_paginate(x, lens, table_np, num_pages, f) for x, f in
+             ((dv["k"], float("nan")), (dv["v"], float("nan")), (kq, 0xCD), (ks, float("nan")))]
+    sm = sm_scale_for(d)
+    kw = dict(max_seq_len=cap, block_size=64, delta=delta, sink=1, local=2, split_blocks=S, sm_scale=sm,
+              pseudo_max=pm)
+    q4 = dev_bf16(qm)
+    nbm = -(-cap // 64)
+    res = []
+    for paged in (False, True):
+        out = torch.empty((B, Q, Hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda")
+        mask = torch.empty((B, Q, Hq, nbm), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(ffd.ffd_decode_multi_workspace_bytes(B, Q, Hq, d, cap, 64, S), dtype=torch.uint8,
+                         device="cuda")
+        io = dict(out=out, lse=lse, kept_mask=mask, workspace=ws)
+        if paged:
+            ffd.ffd_decode_paged_multi(q4, pools[0], pools[1], pools[2], pools[3], table, dv["seq_lens"], **kw, **io)
+        else:
+            ffd.ffd_decode_multi(q4, dv["k"], dv["v"], kq, ks, dv["seq_lens"], **kw, **io)
+        res.append((out, lse, mask))
+    torch.cuda.synchronize()
+    for a, b_, what in zip(res[0], res[1], ("out", "lse", "mask")):
+        assert torch.equal(a, b_), what
+    r_out, r_lse, r_mask = O.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], max_seq_len=cap, block_size=64,
+                                          delta=delta, sink=1, local=2, split_blocks=S, sm_scale=np.float32(sm),
+                                          pseudo_max=pm)
+    assert_mask_equal(res[1][2].cpu().numpy(), r_mask, "mask")
+    assert_close(res[1][0].cpu().numpy().astype(np.float64), r_out, "out")
+    assert_close(res[1][1].cpu().numpy().astype(np.float64), r_lse, "lse")
