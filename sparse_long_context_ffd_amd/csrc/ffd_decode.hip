@@ -202,6 +202,9 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
         constexpr int RB = THUMB ? D / 4 : D / 2;   // code bytes per token
         const uint8_t* kq = (THUMB ? p.k2 : p.kq) + r0 * RB;
         const float* ks = (THUMB ? p.k2scale : p.kscale) + r0;
+        // The int4 sketch is read once: streaming loads. The thumbnail codes
+        // and scales of a kept block are read again by the attend: ordinary
+        // loads, so that the re-read can hit in L2.
 #pragma unroll
         for (int T = 0; T < 4; ++T) {
           const int t = t0 + 16 * T + n;
@@ -210,10 +213,12 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
           if constexpr (RB / 4 == 16) {
             cw[c][T] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
           } else if constexpr (RB / 4 == 8) {
-            const u32x2_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src)) : u32x2_t{0u, 0u};
+            const u32x2_t* s2 = reinterpret_cast<const u32x2_t*>(src);
+            const u32x2_t u = ok ? (THUMB ? *s2 : __builtin_nontemporal_load(s2)) : u32x2_t{0u, 0u};
             cw[c][T] = u32x4_t{u.x, u.y, 0u, 0u};
           } else {
-            const uint32_t u = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src)) : 0u;
+            const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
+            const uint32_t u = ok ? (THUMB ? *s1 : __builtin_nontemporal_load(s1)) : 0u;
             cw[c][T] = u32x4_t{u, 0u, 0u, 0u};
           }
         }
@@ -221,7 +226,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
         // lanes 4T + r of its own 16-lane row: one load per lane, then row
         // broadcasts; tokens past the sequence are not read
         const int tl = 16 * (n >> 2) + 4 * g + (n & 3);
-        scl[c] = t0 + tl < L ? __builtin_nontemporal_load(ks + tl) : 0.f;
+        scl[c] = t0 + tl < L ? (THUMB ? ks[tl] : __builtin_nontemporal_load(ks + tl)) : 0.f;
       }
     }
 #pragma unroll
@@ -455,7 +460,10 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   const float qs = (THUMB && hv) ? sm.qsumf[h] : 0.f;
   __syncthreads();   // the query rows share their space with the V tiles
 
-  for (int e = first; e < nkept; e += stride) {
+  // Kept blocks are taken last-scanned first: on the thumbnail path their
+  // codes, read again here, are then the likeliest to be still in L2.
+  for (int e0 = first; e0 < nkept; e0 += stride) {
+    const int e = nkept - 1 - e0;
     const int jb = j0 + sm.kidx[e];
     const unsigned hm = sm.khm[e];
     const int t0 = jb * kBlockSize;
@@ -491,12 +499,12 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
         }
         const u32x2_t* rs = reinterpret_cast<const u32x2_t*>(p.kr + (r0 + (size_t)(t - t0)) * D + g * (D / 4));
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kres[T][s] = rs[s];
+        for (int s = 0; s < KS; ++s) kres[T][s] = __builtin_nontemporal_load(rs + s);   // read once
       }
       // per-token scales: lane l holds those of row l of the block
       const int tl = min(t0 + lane, tlast) - t0;
       tsl = p.k2scale[r0 + tl];
-      s8l = p.krscale[r0 + tl];
+      s8l = __builtin_nontemporal_load(p.krscale + r0 + tl);
     }
     // The whole V tile is in flight across QK, on the thumbnail path too.
     // (Loading V straight into LDS with global_load_lds_dwordx4 frees its

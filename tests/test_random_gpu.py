@@ -1,6 +1,6 @@
 """Seeded random sweep over the configuration space, every case against the
 oracle (mask bit-exact, out/LSE within the bar): entry point (int4 sketch,
-thumbnail storage, paged cache, several query tokens), group size, head dim,
+thumbnail storage, paged cache, several query tokens, both of the last two), group size, head dim,
 split size up to its maximum of 64 blocks, sink/local counts up to the
 sink/local mode's limit, δ from 0 to +inf, the three pseudo-max modes, bf16 and
 fp32 output, lengths that are empty, a single token, on block boundaries or
@@ -57,6 +57,8 @@ def _case(i):
     cap_extra = int(rng.integers(0, 6))
     if pm == "sink_local" and rng.random() < 0.4:
         pm = "max"   # the larger of the split max and the sink/local estimate
+    if kind == "paged" and rng.random() < 0.5:
+        Q = int(rng.integers(2, 16 // G + 1)) if G < 8 else 2   # several query tokens over the pages
     return dict(kind=kind, B=B, Hq=G * Hkv, Hkv=Hkv, d=d, Q=Q, lens=tuple(lens), S=S, delta=delta, pm=pm,
                 sink=sink, local=local, out_bf16=out_bf16, odd_cap=odd_cap, cap_extra=cap_extra, seed=30_000 + i)
 
@@ -78,6 +80,21 @@ def _pages(x, nbs, table_np, num_pages):
         for jb in range(nbs[b]):
             pool[int(table_np[b, jb])] = x[b, :, 64 * jb:64 * jb + 64]
     return pool
+
+
+def _paged_pools(c, dv, kq, ks, nbm):
+    """The cache rows on shuffled 64-token pages (unused page slots NaN) and the block table."""
+    B = c["B"]
+    nbs = [-(-L // 64) for L in c["lens"]]
+    num_pages = max(1, sum(nbs))
+    perm = np.random.default_rng(c["seed"]).permutation(num_pages)
+    table_np = np.zeros((B, nbm), dtype=np.int32)
+    used = 0
+    for b in range(B):
+        table_np[b, :nbs[b]] = perm[used:used + nbs[b]]
+        used += nbs[b]
+    pools = [_pages(x, nbs, table_np, num_pages) for x in (dv["k"], dv["v"], kq, ks)]
+    return pools, torch.from_numpy(table_np).cuda()
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
@@ -121,23 +138,28 @@ def test_random_case(i):
             r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], storage="thumb", **rkw)
         else:
             kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
-            if c["kind"] == "paged":
-                nbs = [-(-L // 64) for L in c["lens"]]
-                num_pages = max(1, sum(nbs))
-                perm = np.random.default_rng(c["seed"]).permutation(num_pages)
-                table_np = np.zeros((B, nbm), dtype=np.int32)
-                used = 0
-                for b in range(B):
-                    table_np[b, :nbs[b]] = perm[used:used + nbs[b]]
-                    used += nbs[b]
-                pools = [_pages(x, nbs, table_np, num_pages) for x in (dv["k"], dv["v"], kq, ks)]
+            if c["kind"] == "paged" and c["Q"] > 1:
+                pools, table = _paged_pools(c, dv, kq, ks, nbm)
+                Q = c["Q"]
+                qm = multi_query(inp, Q, seed=c["seed"] + 1)
+                out = torch.empty((B, Q, Hq, d), dtype=odt, device="cuda")
+                lse = torch.empty((B, Q, Hq), dtype=torch.float32, device="cuda")
+                mask = torch.empty((B, Q, Hq, nbm), dtype=torch.uint8, device="cuda")
+                ws = torch.empty(ffd.ffd_decode_multi_workspace_bytes(B, Q, Hq, d, cap, 64, c["S"]),
+                                 dtype=torch.uint8, device="cuda")
+                ffd.ffd_decode_paged_multi(dev_bf16(qm), pools[0], pools[1], None if dense else pools[2],
+                                           None if dense else pools[3], table, dv["seq_lens"], out=out, lse=lse,
+                                           kept_mask=mask, workspace=ws, **kw)
+                r_out, r_lse, r_mask = O.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], **rkw)
+            elif c["kind"] == "paged":
+                pools, table = _paged_pools(c, dv, kq, ks, nbm)
                 ffd.ffd_decode_paged(dv["q"], pools[0], pools[1], None if dense else pools[2],
-                                     None if dense else pools[3], torch.from_numpy(table_np).cuda(), dv["seq_lens"],
-                                     **kw, **io)
+                                     None if dense else pools[3], table, dv["seq_lens"], **kw, **io)
+                r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], **rkw)
             else:
                 ffd.ffd_decode(dv["q"], dv["k"], dv["v"], None if dense else kq, None if dense else ks,
                                dv["seq_lens"], **kw, **io)
-            r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], **rkw)
+                r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], **rkw)
     torch.cuda.synchronize()
     assert_mask_equal(mask.cpu().numpy(), r_mask, f"case {i} mask")
     assert_close(out.float().cpu().numpy(), r_out, f"case {i} out", bf16_out=c["out_bf16"])
