@@ -19,6 +19,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--delta D]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -178,6 +179,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the delta=inf comparison")
+    ap.add_argument("--split-blocks", type=int, default=None,
+                    help="blocks per split (the split whose max sets the Top-delta threshold); default: the workload's")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB read+write elementwise kernel (counter calibration)")
     args = ap.parse_args()
@@ -211,6 +214,8 @@ def main() -> int:
         return 0
 
     w = WORKLOADS[args.workload]
+    if args.split_blocks is not None:
+        w = dataclasses.replace(w, split_blocks=args.split_blocks)
     delta = w.deltas[0] if args.delta is None else args.delta
     dense = math.isinf(delta)
     G = w.Hq // w.Hkv
@@ -385,6 +390,11 @@ def main() -> int:
     achieved = alg_bytes / (fused_avg * 1e-6) / 1e9
     value = alg_bytes / (step_us_wall * 1e-6) / 1e9
 
+    # counter summaries are taken in the default split size, one query token
+    traffic = None
+    if Q == 1 and w.split_blocks == WORKLOADS[args.workload].split_blocks:
+        traffic = load_traffic(w.name, delta, {"storage": args.storage, "pseudo_max": args.pseudo_max,
+                                               "paged": bool(args.paged)})
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -421,9 +431,7 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None if Q > 1 else load_traffic(w.name, delta, {"storage": args.storage,
-                                                                         "pseudo_max": args.pseudo_max,
-                                                                         "paged": bool(args.paged)}),
+            "traffic": traffic,
             "algorithmic_bytes_per_launch": int(alg_bytes),
             "avg_launch_us": round(fused_avg, 2),
         },

@@ -662,6 +662,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ DecodeSmem<D, R> sm;
   const int j = blockIdx.y, b = blockIdx.z;
   int split = blockIdx.x, part = 0;
+  // The dispatcher deals workgroups to the 8 XCDs by linear id mod 8, i.e. by
+  // blockIdx.x mod 8 here. Splits past a sequence's end exit at once, so with
+  // ragged lengths a fixed split -> x map loads the XCDs that get the low
+  // splits more; rotating each (sequence, kv head)'s splits by a different
+  // amount spreads every split index over all XCDs.
+  if (p.split_parts == 1) split = (split + b * p.Hkv + j) % p.n_splits;
   if (p.split_parts > 1) {
     // The P workgroups of a split get linear ids 8 apart (the x extent is a
     // multiple of 8), which the dispatcher, dealing workgroups round-robin
