@@ -30,8 +30,8 @@
 //            blocks; then wave 0 compacts the blocks kept by at least one row
 //            into a list (with a per-row bit mask) by ballot. The mask is
 //            stored in the epilogue.
-//  attend    waves take kept blocks round-robin, one 64-token block at a
-//            time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the query
+//  attend    waves take kept blocks round-robin (last-scanned first), one
+//            64-token block at a time, on the matrix cores (v_mfma_f32_16x16x32_bf16, the query
 //            rows padded to 16 columns):
 //              QK  A = K rows straight from HBM into registers (16 tokens x
 //                  32 dims per MFMA; each lane reads D/2 contiguous bytes of a
