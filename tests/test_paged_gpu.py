@@ -114,15 +114,17 @@ def test_paged_dense_path():
     assert_close(lse.cpu().numpy(), r_lse, "paged dense lse")
 
 
-@pytest.mark.parametrize("pm", ["split", "sink_local"])
-def test_paged_full_size_bit_identical(pm):
+@pytest.mark.parametrize("pm,Q", [("split", 1), ("sink_local", 1), ("split", 4)])
+def test_paged_full_size_bit_identical(pm, Q):
     """The 128K x4 workload in the benchmark's paged configuration (shuffled
-    64-token pages): mask, output and LSE bit-identical to the contiguous call,
-    whose parity with the oracle at this size is tested elsewhere."""
-    from ffd_inputs import WORKLOADS, make_inputs
+    64-token pages), with one or four query tokens: mask, output and LSE
+    bit-identical to the contiguous call, whose parity with the oracle at this
+    size is tested elsewhere."""
+    from ffd_inputs import WORKLOADS, make_inputs, multi_query
+    from tests.gpu_util import dev_bf16
 
     w = WORKLOADS["llama3_8b_128k_b4"]
-    say(f"paged full size {w.name} ({pm}): generating")
+    say(f"paged full size {w.name} ({pm}, Q={Q}): generating")
     inp = make_inputs(w)
     dv = to_device(inp)
     B, Hkv, cap, d = dv["k"].shape
@@ -144,19 +146,28 @@ def test_paged_full_size_bit_identical(pm):
     table = table.cuda()
     kw = dict(max_seq_len=cap, block_size=64, delta=w.deltas[0], sink=w.sink, local=w.local,
               split_blocks=w.split_blocks, sm_scale=sm_scale_for(d), pseudo_max=pm)
+    rows = (Q,) if Q > 1 else ()
+    qm = dev_bf16(multi_query(inp, Q, seed=12)) if Q > 1 else None
     res = []
     for paged in (False, True):
-        out = torch.empty((B, w.Hq, d), dtype=torch.float32, device="cuda")
-        lse = torch.empty((B, w.Hq), dtype=torch.float32, device="cuda")
-        mask = torch.empty((B, w.Hq, cap // 64), dtype=torch.uint8, device="cuda")
-        ws = ffd.alloc_workspace(B, w.Hq, d, cap, 64, w.split_blocks)
-        say(f"  {'paged' if paged else 'contiguous'} decode")
-        if paged:
-            ffd.ffd_decode_paged(dv["q"], pools[0], pools[1], pools[2], pools[3], table, dv["seq_lens"], out=out,
-                                 lse=lse, kept_mask=mask, workspace=ws, **kw)
+        out = torch.empty((B,) + rows + (w.Hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B,) + rows + (w.Hq,), dtype=torch.float32, device="cuda")
+        mask = torch.empty((B,) + rows + (w.Hq, cap // 64), dtype=torch.uint8, device="cuda")
+        if Q > 1:
+            ws = torch.empty(ffd.ffd_decode_multi_workspace_bytes(B, Q, w.Hq, d, cap, 64, w.split_blocks),
+                             dtype=torch.uint8, device="cuda")
         else:
-            ffd.ffd_decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], out=out, lse=lse, kept_mask=mask,
-                           workspace=ws, **kw)
+            ws = ffd.alloc_workspace(B, w.Hq, d, cap, 64, w.split_blocks)
+        io = dict(out=out, lse=lse, kept_mask=mask, workspace=ws)
+        say(f"  {'paged' if paged else 'contiguous'} decode")
+        if Q > 1 and paged:
+            ffd.ffd_decode_paged_multi(qm, pools[0], pools[1], pools[2], pools[3], table, dv["seq_lens"], **io, **kw)
+        elif Q > 1:
+            ffd.ffd_decode_multi(qm, dv["k"], dv["v"], kq, ks, dv["seq_lens"], **io, **kw)
+        elif paged:
+            ffd.ffd_decode_paged(dv["q"], pools[0], pools[1], pools[2], pools[3], table, dv["seq_lens"], **io, **kw)
+        else:
+            ffd.ffd_decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], **io, **kw)
         torch.cuda.synchronize()
         res.append((out, lse, mask))
     for a, b_ in zip(res[0], res[1]):
