@@ -249,9 +249,11 @@ size_t ffd_decode_multi_workspace_bytes(int B, int Q, int Hq, int d, int max_seq
  * one contiguous cache per sequence, as serving engines keep it). Pages are laid
  * out as for ffd_quantize_kv_paged (K and V pages bf16 [num_pages, Hkv, 64, d]);
  * block j of sequence b is page block_table[b * table_stride + j], for
- * j < ceil(L / 64); table_stride >= ceil(max_seq_len / 64). Page numbers
- * outside [0, num_pages) are clamped. Same semantics, results and workspace as
- * ffd_decode: a paged cache holding the same rows gives bit-identical outputs.
+ * j < ceil(L / 64); table_stride >= ceil(max_seq_len / 64). num_pages is the
+ * pool's page count (num_pages * Hkv <= 2^31 - 1, else FFD_ERR_UNSUPPORTED);
+ * page numbers outside [0, num_pages) are clamped. Same semantics, results and
+ * workspace as ffd_decode: a paged cache holding the same rows gives
+ * bit-identical outputs.
  */
 ffd_status ffd_decode_paged(const void* q, const void* k_pages, const void* v_pages,
                             const uint8_t* kq_pages, const float* kscale_pages,

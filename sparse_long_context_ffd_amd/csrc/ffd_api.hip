@@ -173,6 +173,9 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
     if (table_stride < nbm)
       return fail(FFD_ERR_INVALID_ARG, "%s: table_stride=%d < ceil(max_seq_len/64)=%ld", fn, table_stride, nbm);
     if (num_pages < 1) return fail(FFD_ERR_INVALID_ARG, "%s: num_pages must be >= 1 (got %d)", fn, num_pages);
+    // the kernel keeps a split's (page, kv head) slot numbers as 32-bit ints
+    if ((long)num_pages * Hkv > 0x7fffffffL)
+      return fail(FFD_ERR_UNSUPPORTED, "%s: num_pages * Hkv = %ld above 2^31 - 1", fn, (long)num_pages * Hkv);
   }
   if (isnan(delta) || delta < 0.f) return fail(FFD_ERR_INVALID_ARG, "%s: delta must be >= 0 (got %g)", fn, (double)delta);
   if (sink_blocks < 0 || local_blocks < 0)

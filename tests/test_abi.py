@@ -137,6 +137,7 @@ def test_paged_multi_validation():
     assert call(None, 4, 10, 2) == ffd.FFD_ERR_INVALID_ARG and "block_table" in ffd.ffd_last_error()
     assert call(fake, 3, 10, 2) == ffd.FFD_ERR_INVALID_ARG and "table_stride" in ffd.ffd_last_error()
     assert call(fake, 4, 0, 2) == ffd.FFD_ERR_INVALID_ARG and "num_pages" in ffd.ffd_last_error()
+    assert call(fake, 4, 2 ** 30, 2, Hq=8, Hkv=2) == ffd.FFD_ERR_UNSUPPORTED and "num_pages" in ffd.ffd_last_error()
     assert call(fake, 4, 10, 0) == ffd.FFD_ERR_INVALID_ARG and "Q=0" in ffd.ffd_last_error()
     assert call(fake, 4, 10, 5, Hq=4, Hkv=1) == ffd.FFD_ERR_UNSUPPORTED
     assert "ffd_decode_paged_multi" in ffd.ffd_last_error()
