@@ -19,7 +19,7 @@ from tests.gpu_util import assert_close, assert_mask_equal, dev_bf16, say, sm_sc
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 256
+N_CASES = 1024
 
 
 def _case(i):
