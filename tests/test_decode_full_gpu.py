@@ -50,3 +50,33 @@ def test_full_size(name):
             assert_mask_equal(mask[b, h], r_mask2[b, h], f"{name} mask b={b} h={h}")
             assert_close(out[b, h], r_out[b, h], f"{name} out b={b} h={h} delta={delta}")
             assert_close(lse[b, h], r_lse[b, h], f"{name} lse b={b} h={h} delta={delta}")
+
+
+@pytest.fixture(scope="module")
+def longest_inputs():
+    from ffd_inputs import make_random_inputs
+
+    L = (1 << 20) + 37
+    say(f"longest sequence L={L}: generating")
+    inp = make_random_inputs(1, 8, 1, 128, (L,), seed=4242, block_size=64, hot_frac=0.01)
+    return inp, to_device(inp)
+
+
+@pytest.mark.parametrize("pm", ["split", "max"])
+def test_longest_sequence_widest_split(pm, longest_inputs):
+    """Sizes at the top of what one call handles in one piece: a single
+    sequence of 2^20 + 37 tokens (16385 blocks, a ragged last block), the
+    widest split (64 blocks), eight query heads on one kv head, and many sink
+    and local blocks; mask bit-exact on every head, output and LSE on all."""
+    inp, dv = longest_inputs
+    say(f"longest sequence, S=64, {pm}: GPU")
+    sm = sm_scale_for(128)
+    kw = dict(max_seq_len=inp["cap"], delta=2.0, sink=4, local=12, split_blocks=64, pseudo_max=pm)
+    out, lse, mask = run_gpu(dv, sm_scale=sm, **kw)
+    say(f"  kept fraction {mask.mean():.4f}; oracle")
+    r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], block_size=64,
+                                    sm_scale=np.float32(sm), **kw)
+    assert 0.0 < mask.mean() < 1.0
+    assert_mask_equal(mask, r_mask, f"longest sequence mask ({pm})")
+    assert_close(out, r_out, f"longest sequence out ({pm})")
+    assert_close(lse, r_lse, f"longest sequence lse ({pm})")
