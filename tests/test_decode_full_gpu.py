@@ -80,3 +80,25 @@ def test_longest_sequence_widest_split(pm, longest_inputs):
     assert_mask_equal(mask, r_mask, f"longest sequence mask ({pm})")
     assert_close(out, r_out, f"longest sequence out ({pm})")
     assert_close(lse, r_lse, f"longest sequence lse ({pm})")
+
+
+def test_many_short_sequences():
+    """A wide batch: 300 sequences of 0 to 3000 tokens (empty ones included)
+    in one call, against the oracle on every row."""
+    from ffd_inputs import make_random_inputs
+
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 3001, size=300)
+    lens[::37] = 0
+    say(f"many short sequences: B={len(lens)}, {int(lens.sum())} tokens")
+    inp = make_random_inputs(len(lens), 8, 2, 64, tuple(int(x) for x in lens), seed=78, block_size=64,
+                             hot_frac=0.05)
+    dv = to_device(inp)
+    sm = sm_scale_for(64)
+    kw = dict(max_seq_len=inp["cap"], delta=1.0, sink=1, local=2, split_blocks=8)
+    out, lse, mask = run_gpu(dv, sm_scale=sm, **kw)
+    r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], block_size=64,
+                                    sm_scale=np.float32(sm), **kw)
+    assert_mask_equal(mask, r_mask, "many sequences mask")
+    assert_close(out, r_out, "many sequences out")
+    assert_close(lse, r_lse, "many sequences lse")
