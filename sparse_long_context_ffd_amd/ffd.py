@@ -148,6 +148,13 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
                          f"{tuple(t.shape)} {t.dtype} contiguous={t.is_contiguous()} device={t.device}")
 
 
+def _need_per_seq(t: torch.Tensor, name: str, B: int) -> None:
+    """An int32 vector with one entry per sequence."""
+    _need(t, name, torch.int32, 1)
+    if t.shape[0] != B:
+        raise ValueError(f"{name} needs one entry per sequence ({B}), got {t.shape[0]}")
+
+
 def ffd_decode_workspace_bytes(B: int, Hq: int, d: int, max_seq_len: int, block_size: int = 64,
                                split_blocks: int = 32) -> int:
     return int(lib().ffd_decode_workspace_bytes(B, Hq, d, max_seq_len, block_size, split_blocks))
@@ -274,7 +281,7 @@ def ffd_combine(seq_lens, *, max_seq_len: int, block_size: int, split_blocks: in
                 out: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
     """Log-sum-exp merge of the per-split partials in ``workspace`` into ``out`` / ``lse``."""
     B, Hq, d = out.shape
-    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need_per_seq(seq_lens, "seq_lens", B)
     odt = _check_outputs(out, lse, B, Hq, d)
     _check(lib().ffd_combine(_ptr(seq_lens), int(max_seq_len), B, Hq, d, int(block_size), int(split_blocks),
                              _ptr(workspace), _ws(workspace), _ptr(out), odt, _ptr(lse), _stream(stream)))
@@ -294,8 +301,31 @@ def ffd_quantize_kv_paged(k_pages: torch.Tensor, kq_pages: torch.Tensor, kscale_
     if tuple(kq_pages.shape) != (P, Hkv, 64, d // 2) or tuple(kscale_pages.shape) != (P, Hkv, 64):
         raise ValueError("kq/kscale page shapes do not match k_pages")
     B, stride = block_table.shape
+    _need_per_seq(pos_begin, "pos_begin", B)
+    _need_per_seq(pos_end, "pos_end", B)
     _check(lib().ffd_quantize_kv_paged(_ptr(k_pages), _ptr(kq_pages), _ptr(kscale_pages), _ptr(block_table), stride,
                                        P, _ptr(pos_begin), _ptr(pos_end), B, Hkv, d, int(max_span), _stream(stream)))
+
+
+def _check_pages(k_pages, v_pages, kq_pages, kscale_pages, block_table, seq_lens, B: int, d: int):
+    """Shapes of a page pool and its block table; returns (num_pages, Hkv)."""
+    _need(k_pages, "k_pages", torch.bfloat16, 4)
+    _need(v_pages, "v_pages", torch.bfloat16, 4)
+    P, Hkv, bs, _ = k_pages.shape
+    if bs != 64 or tuple(k_pages.shape) != (P, Hkv, 64, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("k/v pages must be [num_pages, Hkv, 64, d]")
+    _need(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[0] != B:
+        raise ValueError("block_table needs one row per sequence")
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens needs one entry per sequence")
+    if kq_pages is not None:
+        _need(kq_pages, "kq_pages", torch.uint8, 4)
+        _need(kscale_pages, "kscale_pages", torch.float32, 3)
+        if tuple(kq_pages.shape) != (P, Hkv, 64, d // 2) or tuple(kscale_pages.shape) != (P, Hkv, 64):
+            raise ValueError("kq/kscale pages must be [num_pages, Hkv, 64, d/2] and [num_pages, Hkv, 64]")
+    return P, Hkv
 
 
 def ffd_decode_paged(q, k_pages, v_pages, kq_pages, kscale_pages, block_table, seq_lens, *, max_seq_len: int,
@@ -304,19 +334,8 @@ def ffd_decode_paged(q, k_pages, v_pages, kq_pages, kscale_pages, block_table, s
                      workspace: Optional[torch.Tensor], pseudo_max: str = "split", stream=None) -> None:
     """One decode step over a paged cache into preallocated outputs."""
     _need(q, "q", torch.bfloat16, 3)
-    _need(k_pages, "k_pages", torch.bfloat16, 4)
-    _need(v_pages, "v_pages", torch.bfloat16, 4)
     B, Hq, d = q.shape
-    P, Hkv, bs, _ = k_pages.shape
-    if bs != 64 or tuple(k_pages.shape) != (P, Hkv, 64, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
-        raise ValueError("k/v pages must be [num_pages, Hkv, 64, d]")
-    _need(block_table, "block_table", torch.int32, 2)
-    if block_table.shape[0] != B:
-        raise ValueError("block_table needs one row per sequence")
-    _need(seq_lens, "seq_lens", torch.int32, 1)
-    if kq_pages is not None:
-        _need(kq_pages, "kq_pages", torch.uint8, 4)
-        _need(kscale_pages, "kscale_pages", torch.float32, 3)
+    P, Hkv = _check_pages(k_pages, v_pages, kq_pages, kscale_pages, block_table, seq_lens, B, d)
     if kept_mask is not None:
         _need(kept_mask, "kept_mask", torch.uint8, 3)
         if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
@@ -339,19 +358,8 @@ def ffd_decode_paged_multi(q, k_pages, v_pages, kq_pages, kscale_pages, block_ta
     into preallocated ``out`` ``[B, Q, Hq, d]`` / ``lse`` ``[B, Q, Hq]`` /
     ``kept_mask`` ``[B, Q, Hq, NB]``."""
     _need(q, "q", torch.bfloat16, 4)
-    _need(k_pages, "k_pages", torch.bfloat16, 4)
-    _need(v_pages, "v_pages", torch.bfloat16, 4)
     B, Q, Hq, d = q.shape
-    P, Hkv, bs, _ = k_pages.shape
-    if bs != 64 or tuple(k_pages.shape) != (P, Hkv, 64, d) or tuple(v_pages.shape) != tuple(k_pages.shape):
-        raise ValueError("k/v pages must be [num_pages, Hkv, 64, d]")
-    _need(block_table, "block_table", torch.int32, 2)
-    if block_table.shape[0] != B:
-        raise ValueError("block_table needs one row per sequence")
-    _need(seq_lens, "seq_lens", torch.int32, 1)
-    if kq_pages is not None:
-        _need(kq_pages, "kq_pages", torch.uint8, 4)
-        _need(kscale_pages, "kscale_pages", torch.float32, 3)
+    P, Hkv = _check_pages(k_pages, v_pages, kq_pages, kscale_pages, block_table, seq_lens, B, d)
     if kept_mask is not None:
         _need(kept_mask, "kept_mask", torch.uint8, 4)
         if tuple(kept_mask.shape) != (B, Q, Hq, -(-max_seq_len // block_size)):
@@ -378,6 +386,8 @@ def ffd_quantize_kv_thumb(k, k2, k2scale, kr, krscale, pos_begin, pos_end, max_s
     if (tuple(k2.shape) != (B, Hkv, cap, d // 4) or tuple(kr.shape) != (B, Hkv, cap, d)
             or tuple(k2scale.shape) != (B, Hkv, cap) or tuple(krscale.shape) != (B, Hkv, cap)):
         raise ValueError("thumbnail/residual shapes do not match k")
+    _need_per_seq(pos_begin, "pos_begin", B)
+    _need_per_seq(pos_end, "pos_end", B)
     _check(lib().ffd_quantize_kv_thumb(_ptr(k), _ptr(k2), _ptr(k2scale), _ptr(kr), _ptr(krscale), _ptr(pos_begin),
                                        _ptr(pos_end), B, Hkv, cap, d, int(max_span), _stream(stream)))
 
@@ -396,9 +406,10 @@ def ffd_decode_thumb(q, k2, k2scale, kr, krscale, v, seq_lens, *, max_seq_len: i
     _need(kr, "kr", torch.int8, 4)
     _need(krscale, "krscale", torch.float32, 3)
     if (tuple(k2.shape) != (B, Hkv, cap, d // 4) or tuple(kr.shape) != (B, Hkv, cap, d)
-            or tuple(v.shape) != (B, Hkv, cap, d)):
+            or tuple(v.shape) != (B, Hkv, cap, d) or tuple(k2scale.shape) != (B, Hkv, cap)
+            or tuple(krscale.shape) != (B, Hkv, cap)):
         raise ValueError("thumbnail/residual/v shapes do not match q")
-    _need(seq_lens, "seq_lens", torch.int32, 1)
+    _need_per_seq(seq_lens, "seq_lens", B)
     if kept_mask is not None:
         _need(kept_mask, "kept_mask", torch.uint8, 3)
         if tuple(kept_mask.shape) != (B, Hq, -(-max_seq_len // block_size)):
