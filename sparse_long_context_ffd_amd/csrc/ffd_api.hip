@@ -252,6 +252,7 @@ ffd_status prepare_decode(const char* fn, const void* q, const void* k, const vo
   p.nb_max = nb_max;
   p.n_splits = ns;
   p.split_parts = parts;
+  p.waves = ns > 0 ? ffd::waves_for(B, Hq, ns) : 4;
   p.split_blocks = split_blocks;
   p.sink = sink_blocks;
   p.local = local_blocks;
@@ -493,6 +494,7 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   p.nb_max = nb_max_for(max_seq_len);
   p.n_splits = ns;
   p.split_parts = parts;
+  p.waves = ns > 0 ? ffd::waves_for(B, Hq, ns) : 4;
   p.split_blocks = split_blocks;
   return launch(fn, p, d, 1, false, ffd::Stage::kCombine, stream);
 }

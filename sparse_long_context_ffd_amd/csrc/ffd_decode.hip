@@ -58,20 +58,18 @@ namespace ffd {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 
 // R query rows per workgroup: R = G heads of the kv group for one query token,
 // or G x Q for Q query tokens (row r = token r / G, head r % G).
-template <int D, int R>
+template <int D, int R, int NW>
 struct DecodeSmem {
   // The V tiles are live only during attend: the bf16 query rows (read into
   // registers at its start) and the epilogue's per-wave partial outputs reuse
   // their space.
   union alignas(16) {
-    uint16_t vt[kWaves][kBlockSize * D];  // per-wave V tile (bf16, swizzled rows)
+    uint16_t vt[NW][kBlockSize * D];      // per-wave V tile (bf16, swizzled rows)
     uint16_t qb[R][D];                    // bf16 query rows
-    float wo[kWaves][R][D];               // per-wave partial outputs (epilogue)
+    float wo[NW][R][D];                   // per-wave partial outputs (epilogue)
   };
   alignas(16) int8_t qc[R][D];  // int8 scan query
   static_assert(sizeof(float) * R <= sizeof(uint16_t) * kBlockSize, "wave partials must fit the V tiles");
@@ -88,11 +86,11 @@ struct DecodeSmem {
   uint8_t kidx[kMaxSplit];  // kept blocks (split-local index)
   uint16_t khm[kMaxSplit];  // per-row keep bits of each kept block
   uint16_t hmb[kMaxSplit];  // per-row keep bits of every block of the split (mask)
-  uint16_t hmw[kWaves][kMaxSplit];  // the same, for the rows of each wave
+  uint16_t hmw[NW][kMaxSplit];  // the same, for the rows of each wave
   int nkept;
-  float wm[kWaves][R];
-  float wl[kWaves][R];
-  float wa[kWaves][R];      // epilogue: each wave's weight in the row's merge
+  float wm[NW][R];
+  float wl[NW][R];
+  float wa[NW][R];          // epilogue: each wave's weight in the row's merge
   float rlse[R];            // epilogue: the row's natural-log LSE
 };
 
@@ -124,8 +122,8 @@ __device__ __forceinline__ int row_len(const DecodeParams& p, int sl, int r) {
 // First cache row of block jb of (sequence b, kv head j). For a paged cache
 // the split's rows were looked up once into LDS (rowp); blocks outside the
 // split (sink/local pseudo-max) read the block table directly.
-template <int D, int R>
-__device__ __forceinline__ size_t block_row(const DecodeParams& p, const DecodeSmem<D, R>& sm, int b, int j, int j0,
+template <int D, int R, int NW>
+__device__ __forceinline__ size_t block_row(const DecodeParams& p, const DecodeSmem<D, R, NW>& sm, int b, int j, int j0,
                                             int nblk, int jb) {
   if (p.block_table != nullptr && jb >= j0 && jb < j0 + nblk) return (size_t)(unsigned)sm.rowp[jb - j0] * kBlockSize;
   return cache_block_row(p.block_table, p.table_stride, p.num_pages, p.cap, p.Hkv, b, j, jb);
@@ -168,8 +166,8 @@ __device__ __forceinline__ int scan_rotation(const DecodeParams& p, int j0, int 
   return (p.block_table != nullptr && nblk > 0) ? (j0 / p.split_blocks) % nblk : 0;
 }
 
-template <int D, int G, int QT, bool THUMB>
-__device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
+template <int D, int G, int QT, bool THUMB, int NW>
+__device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
                                                int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
   constexpr int R = G * QT;
   constexpr int NM = D / 64;   // MFMAs per tile (k = 64 each)
@@ -201,12 +199,12 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
 
   constexpr int kChunk = 4;
   const int rot = scan_rotation(p, j0, nblk_split);
-  for (int jc = w; jc < nblk; jc += kWaves * kChunk) {
+  for (int jc = w; jc < nblk; jc += NW * kChunk) {
     u32x4_t cw[kChunk][4];
     float scl[kChunk];   // lane (g, n): scale of token 16 * (n / 4) + 4g + n % 4 of the block
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const int jl = jc + c * kWaves;
+      const int jl = jc + c * NW;
       if (jl < nblk) {
         int jp = jl + rot;   // the split's blocks in rotated order
         if (jp >= nblk_split) jp -= nblk_split;
@@ -245,7 +243,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
     }
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const int jl = jc + c * kWaves;
+      const int jl = jc + c * NW;
       if (jl >= nblk) continue;
       int jp = jl + rot;
       if (jp >= nblk_split) jp -= nblk_split;
@@ -308,15 +306,15 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
 // extra ones scanned outside the split first), or the larger of the two; the
 // threshold fl32(pm - δ), the forced blocks; the row's keep bits go to LDS
 // per wave.
-template <int D, int G, int QT>
-__device__ __forceinline__ void select_rows(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int j0, int nblk,
+template <int D, int G, int QT, int NW>
+__device__ __forceinline__ void select_rows(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int j0, int nblk,
                                             int nx, int sl, int lane, int w) {
   constexpr int R = G * QT;
   const int jl = lane;
   const int jb = j0 + jl;
   const bool in_split = jl < nblk;
   unsigned hm = 0;
-  for (int r = w; r < R; r += kWaves) {
+  for (int r = w; r < R; r += NW) {
     const int NBr = (row_len<G>(p, sl, r) + kBlockSize - 1) / kBlockSize;
     float pm = 0.f;
     if (p.pm_sink_local) {
@@ -344,8 +342,8 @@ __device__ __forceinline__ void select_rows(const DecodeParams& p, DecodeSmem<D,
 // The kept list (one wave, lane = block): blocks kept by at least one row,
 // compacted by ballot, each with its per-row keep bits; hm also goes to LDS
 // for the mask, which is written in the epilogue.
-template <int D, int R>
-__device__ __forceinline__ void compact_kept(DecodeSmem<D, R>& sm, unsigned hm, int lane) {
+template <int D, int R, int NW>
+__device__ __forceinline__ void compact_kept(DecodeSmem<D, R, NW>& sm, unsigned hm, int lane) {
   sm.hmb[lane] = (uint16_t)hm;
   const unsigned long long bal = __ballot(hm != 0u);
   const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
@@ -414,11 +412,11 @@ struct AttendState {
 // (the longest row), which bounds every load.
 // Kept blocks first, first + stride, ... are this wave's; its V tile is the
 // one of wave w of the workgroup.
-template <int D, int G, int QT, bool DENSE, bool THUMB>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G * QT>& sm, int b, int j,
+template <int D, int G, int QT, bool DENSE, bool THUMB, int NW>
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
                                               int j0, int L, int Lrow, int lane, int first, int stride,
                                               AttendState<D>& st) {
-  const int w = first % kWaves;
+  const int w = first % NW;
   constexpr int R = G * QT;
   constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
   constexpr int NT = D / 16;    // MFMA n-tiles of the output
@@ -670,14 +668,18 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, flo
 
 // One workgroup per (split, kv head j, sequence b) serving R = G x QT query
 // rows: the G heads of the group for each of the (up to QT) query tokens.
-template <int D, int G, int QT, bool DENSE, bool THUMB>
-// Two waves per SIMD: the LDS of two workgroups per CU allows no more, and
-// the registers must not allow fewer.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fused_decode_kernel(
+// NW waves per workgroup: 4 (two workgroups per CU), or 8 on small grids (one
+// per CU, each wave scanning and attending half as many blocks).
+template <int D, int G, int QT, bool DENSE, bool THUMB, int NW>
+// Two waves per SIMD: the LDS of the workgroups that fit a CU allows no more,
+// and the registers must not allow fewer.
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void fused_decode_kernel(
     const DecodeParams p) {
   constexpr int R = G * QT;
+  constexpr int kThreads = 64 * NW;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   static_assert(QT == 1 || !THUMB, "several query tokens only with the int4 sketch");
-  __shared__ DecodeSmem<D, R> sm;
+  __shared__ DecodeSmem<D, R, NW> sm;
   const int j = blockIdx.y, b = blockIdx.z;
   int split = blockIdx.x, part = 0;
   // The dispatcher deals workgroups to the 8 XCDs by linear id mod 8, i.e. by
@@ -788,14 +790,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // sink/local pseudo-max: the sink and local blocks outside this split are
     // listed in the prologue and scanned in the same pass as the split
     const int nx = p.pm_sink_local ? sm.nx : 0;
-    scan_blocks_mq<D, G, QT, THUMB>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
+    scan_blocks_mq<D, G, QT, THUMB, NW>(p, sm, b, j, j0, nblk, nx, L, sl, lane, w);
     __syncthreads();
-    select_rows<D, G, QT>(p, sm, j0, nblk, nx, sl, lane, w);
+    select_rows<D, G, QT, NW>(p, sm, j0, nblk, nx, sl, lane, w);
     __syncthreads();
     if (w == 0) {
       unsigned hm = 0;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) hm |= sm.hmw[ww][lane];
+      for (int ww = 0; ww < NW; ++ww) hm |= sm.hmw[ww][lane];
       compact_kept(sm, hm, lane);
     }
   } else {
@@ -812,8 +814,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // ---- attend -------------------------------------------------------------
   AttendState<D> st;
-  attend_blocks<D, G, QT, DENSE, THUMB>(p, sm, b, j, j0, L, row_len<G>(p, sl, lane & 15), lane,
-                                        part * kWaves + w, kWaves * p.split_parts, st);
+  attend_blocks<D, G, QT, DENSE, THUMB, NW>(p, sm, b, j, j0, L, row_len<G>(p, sl, lane & 15), lane,
+                                        part * NW + w, NW * p.split_parts, st);
 
   // this wave's partial: normaliser of row h summed over its 4 lane groups;
   // the partial outputs overwrite the V tiles, so every wave must be done
@@ -844,17 +846,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int h = tid;
     float mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, sm.wm[ww][h]);
-    float a[kWaves], den = 0.f;
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm.wm[ww][h]);
+    float a[NW], den = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       a[ww] = (sm.wm[ww][h] == -INFINITY) ? 0.f : exp2f(sm.wm[ww][h] - mx);
       den += sm.wl[ww][h] * a[ww];
     }
     // a row can keep no block of a split (sink/local pseudo-max, or a query
     // token that does not see the split): empty partial, weight 0
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) sm.wa[ww][h] = den > 0.f ? a[ww] / den : 0.f;
+    for (int ww = 0; ww < NW; ++ww) sm.wa[ww][h] = den > 0.f ? a[ww] / den : 0.f;
     sm.rlse[h] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
   }
   __syncthreads();
@@ -864,7 +866,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     if (h / G >= p.Q) continue;
     f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sm.wo[ww][h][cc]);
       const float a = sm.wa[ww][h];
 #pragma unroll
@@ -982,7 +984,10 @@ hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) 
   if ((static_cast<int>(stage) & static_cast<int>(Stage::kPartials)) && p.n_splits > 0) {
     const int gx = p.split_parts == 1 ? p.n_splits : (p.n_splits + 7) / 8 * 8 * p.split_parts;
     dim3 grid(gx, p.Hkv, p.B);
-    fused_decode_kernel<D, G, QT, DENSE, THUMB><<<grid, kThreads, 0, stream>>>(p);
+    if (p.waves == 8)
+      fused_decode_kernel<D, G, QT, DENSE, THUMB, 8><<<grid, 512, 0, stream>>>(p);
+    else
+      fused_decode_kernel<D, G, QT, DENSE, THUMB, 4><<<grid, 256, 0, stream>>>(p);
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
     combine_kernel<D><<<dim3(p.Q * p.Hq, p.B, D / kCombineDims), kCombineThreads, 0, stream>>>(p);

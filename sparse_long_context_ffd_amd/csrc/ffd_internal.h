@@ -14,6 +14,16 @@ constexpr int kMaxRows = 16;     // query rows (query tokens x heads of a kv gro
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxParts = 4;     // workgroups sharing one split's attend work
 
+// Waves per workgroup. On a grid of fewer than 1024 (sequence, query head,
+// split) units -- under two 4-wave workgroups per CU at G = 4 -- the kernel
+// runs 8 waves per workgroup, one workgroup per CU: each wave then has half
+// the scan and attend blocks, which halves the latency chain of a grid that
+// is one round long.
+inline int waves_for(int B, int Hq, int n_splits) {
+  const long units = (long)B * Hq * n_splits;
+  return units > 0 && units < 1024 ? 8 : 4;
+}
+
 // Workgroups per split. When (sequence, kv head, split) units are too few to
 // fill the chip, P workgroups share a split: each scans and selects the whole
 // split (same kept set) and attends every P-th kept block, leaving one
@@ -21,8 +31,8 @@ constexpr int kMaxParts = 4;     // workgroups sharing one split's attend work
 // and a separate combine call agree with the decode.
 inline int split_parts_for(int B, int Hq, int n_splits) {
   const long units = (long)B * Hq * n_splits;
-  if (units <= 0) return 1;
-  const long P = 2048 / units;   // about one round of resident workgroups at G = 4
+  if (units <= 0 || waves_for(B, Hq, n_splits) == 4) return 1;
+  const long P = 1024 / units;   // about one round of resident 8-wave workgroups at G = 4
   return P < 1 ? 1 : (P > kMaxParts ? kMaxParts : (int)P);
 }
 
@@ -51,6 +61,7 @@ struct DecodeParams {
   int nb_max;              // ceil(max_seq_len / kBlockSize)
   int n_splits;            // ceil(nb_max / split_blocks)
   int split_parts;         // workgroups per split (split_parts_for); partials per row = n_splits * split_parts
+  int waves;               // waves per workgroup (waves_for): 4 or 8
   int split_blocks;
   int sink, local;
   int pm_sink_local;       // 1: pseudo-max over the sink/local blocks; 0: split max

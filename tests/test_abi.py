@@ -167,7 +167,10 @@ def _decode_multi(**kw):
 
 def _ws_expected(B, rows, Hq, L, S, d):
     ns = -(-(-(-L // 64)) // S)
-    parts = min(4, max(1, 2048 // (B * Hq * ns)))   # workgroups per split
+    units = B * Hq * ns
+    # workgroups per split: one, or on grids of under 1024 units (8-wave
+    # workgroups) up to four, about one round of them
+    parts = min(4, max(1, 1024 // units)) if units < 1024 else 1
     n = B * rows * ns * parts
     return -(-n * d * 4 // 256) * 256 + -(-n * 4 // 256) * 256
 
@@ -181,9 +184,12 @@ def test_multi_workspace_bytes():
 
 
 def test_small_grids_get_more_partials():
-    # 32K tokens, one sequence: 16 splits x 32 heads -> 4 workgroups per split
+    # 32K tokens, one sequence: 16 splits x 32 heads = 512 units -> 2 workgroups per split
     assert ffd.ffd_decode_workspace_bytes(1, 32, 128, 32768, 64, 32) == _ws_expected(1, 32, 32, 32768, 32, 128)
-    assert _ws_expected(1, 32, 32, 32768, 32, 128) > 4 * 32 * 16 * 128 * 3
+    assert _ws_expected(1, 32, 32, 32768, 32, 128) >= 2 * 32 * 16 * 128 * 4
+    # 128K x4: 8192 units -> one workgroup per split
+    assert ffd.ffd_decode_workspace_bytes(4, 32, 128, 131072, 64, 32) == _ws_expected(4, 32, 32, 131072, 32, 128)
+    assert _ws_expected(4, 32, 32, 131072, 32, 128) < 2 * 4 * 32 * 64 * 128 * 4
 
 
 @pytest.mark.parametrize("kw,status,needle", [
