@@ -304,10 +304,11 @@ ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2sca
  * as ffd_decode (the kept_mask is written here); instead of the final output
  * it leaves every split's partial results in the workspace:
  *   n_splits = ceil(ceil(max_seq_len / block_size) / split_blocks)
- *   P        = clamp(floor(2048 / (B * Hq * n_splits)), 1, 4): workgroups
- *              per split when the grid alone would leave the chip idle;
- *              each scans and selects the whole split (one kept set) and
- *              attends every P-th kept block
+ *   units    = B * Hq * n_splits
+ *   P        = clamp(floor(1024 / units), 1, 4) if units < 1024, else 1:
+ *              workgroups per split when the grid alone would leave the
+ *              chip idle; each scans and selects the whole split (one kept
+ *              set) and attends every P-th kept block
  *   o_part   f32 [B, Hq, n_splits, P, d] at byte offset 0: each part's
  *            attention output, normalised over the kept tokens it attended
  *   lse_part f32 [B, Hq, n_splits, P] at byte offset
