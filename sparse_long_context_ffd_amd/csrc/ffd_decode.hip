@@ -7,10 +7,10 @@
 // the kept blocks) run in ONE kernel per (sequence, kv head, split), so the
 // kept set never leaves the workgroup ([TS] Methodology 3, "Fused Kernel").
 //
-// One workgroup = 4 wave64s owns `split_blocks` consecutive 64-token blocks of
-// one (sequence b, kv head j) and serves all G = Hq/Hkv query heads of the
-// group -- for Q query tokens per sequence, G x Q query rows -- so every K/V
-// byte it reads is shared by all of them. When the grid is too small to fill
+// One workgroup = 4 wave64s (8 on grids one round long) owns `split_blocks`
+// consecutive 64-token blocks of one (sequence b, kv head j) and serves all
+// G = Hq/Hkv query heads of the group -- for Q query tokens per sequence,
+// G x Q query rows -- so every K/V byte it reads is shared by all of them. When the grid is too small to fill
 // the chip, P workgroups share a split (each scans and selects all of it and
 // attends every P-th kept block).
 //
@@ -300,7 +300,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
 // ---------------------------------------------------------------------------
 // Row r (query token r / G, head r % G) sees NB_r blocks; a block it cannot see
 // is never kept for it, and its sink/local blocks are those of its own range.
-// Wave w takes rows w, w + 4, ...; lane = block of the split. Per row: the
+// Wave w takes rows w, w + NW, ...; lane = block of the split. Per row: the
 // split max m~ (the seed of its softmax, and the pseudo-max in split mode),
 // the sink/local estimate (max over the row's own sink and local blocks, the
 // extra ones scanned outside the split first), or the larger of the two; the
