@@ -305,7 +305,7 @@ ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2sca
  * it leaves every split's partial results in the workspace:
  *   n_splits = ceil(ceil(max_seq_len / block_size) / split_blocks)
  *   units    = B * Hq * n_splits
- *   P        = clamp(floor(1024 / units), 1, 4) if units < 1024, else 1:
+ *   P        = clamp(floor(1024 / units), 1, 4) if units <= 1024, else 1:
  *              workgroups per split when the grid alone would leave the
  *              chip idle; each scans and selects the whole split (one kept
  *              set) and attends every P-th kept block

@@ -14,14 +14,14 @@ constexpr int kMaxRows = 16;     // query rows (query tokens x heads of a kv gro
 constexpr size_t kWsAlign = 256;
 constexpr int kMaxParts = 4;     // workgroups sharing one split's attend work
 
-// Waves per workgroup. On a grid of fewer than 1024 (sequence, query head,
-// split) units -- under two 4-wave workgroups per CU at G = 4 -- the kernel
+// Waves per workgroup. On a grid of at most 1024 (sequence, query head,
+// split) units -- at most one 4-wave workgroup per CU at G = 4 -- the kernel
 // runs 8 waves per workgroup, one workgroup per CU: each wave then has half
 // the scan and attend blocks, which halves the latency chain of a grid that
 // is one round long.
 inline int waves_for(int B, int Hq, int n_splits) {
   const long units = (long)B * Hq * n_splits;
-  return units > 0 && units < 1024 ? 8 : 4;
+  return units > 0 && units <= 1024 ? 8 : 4;
 }
 
 // Workgroups per split. When (sequence, kv head, split) units are too few to

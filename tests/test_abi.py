@@ -168,9 +168,9 @@ def _decode_multi(**kw):
 def _ws_expected(B, rows, Hq, L, S, d):
     ns = -(-(-(-L // 64)) // S)
     units = B * Hq * ns
-    # workgroups per split: one, or on grids of under 1024 units (8-wave
+    # workgroups per split: one, or on grids of at most 1024 units (8-wave
     # workgroups) up to four, about one round of them
-    parts = min(4, max(1, 1024 // units)) if units < 1024 else 1
+    parts = min(4, max(1, 1024 // units)) if units <= 1024 else 1
     n = B * rows * ns * parts
     return -(-n * d * 4 // 256) * 256 + -(-n * 4 // 256) * 256
 
