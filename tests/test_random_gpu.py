@@ -97,9 +97,38 @@ def _paged_pools(c, dv, kq, ks, nbm):
     return pools, torch.from_numpy(table_np).cuda()
 
 
+def _case_four_waves(i):
+    """A case on a grid of more than 1024 (sequence, query head, split) units,
+    where the kernel runs 4-wave workgroups (smaller grids run 8-wave ones):
+    three ragged sequences, 16 or 32 query heads, one-block splits."""
+    rng = np.random.default_rng(40_000 + i)
+    kind = ["int4", "thumb", "paged", "multi"][i % 4]
+    G = int(rng.choice([2, 4, 8]))
+    Hkv = 8 if G == 2 else 4
+    d = int(rng.choice([64, 128]))
+    Q = (int(rng.integers(2, 16 // G + 1)) if G < 8 else 2) if kind == "multi" else 1
+    lens = tuple(int(x) for x in rng.integers(1500, 4000, size=3))
+    delta = float(rng.choice([0.0, 1.0, 2.0, 4.0, math.inf]))
+    pm = str(rng.choice(["split", "sink_local", "max"])) if not math.isinf(delta) else "split"
+    sink, local = int(rng.integers(0, 3)), int(rng.integers(1, 5))
+    c = dict(kind=kind, B=3, Hq=G * Hkv, Hkv=Hkv, d=d, Q=Q, lens=lens, S=1, delta=delta, pm=pm, sink=sink,
+             local=local, out_bf16=bool(rng.random() < 0.25), odd_cap=False, cap_extra=0, seed=45_000 + i)
+    ns = -(-max(lens) // 64)
+    assert c["B"] * c["Hq"] * ns > 1024
+    return c
+
+
+@pytest.mark.parametrize("i", range(64))
+def test_random_case_four_waves(i):
+    _run_case(_case_four_waves(i), f"4-wave {i}")
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(i):
-    c = _case(i)
+    _run_case(_case(i), str(i))
+
+
+def _run_case(c, i):
     if c["pm"] != "split" and c["sink"] + c["local"] + (c["Q"] > 1) > 64:
         c["local"] -= 1
     say(f"random case {i}: {c}")
