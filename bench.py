@@ -251,7 +251,12 @@ def main() -> int:
             return 2
         k2, k2s, kr, krs = ffd.quantize_kv_thumb(k, seq)
         del kq, ks
+        # the thumbnail build, timed like the int4 one (a second, warm call)
+        qb0.record()
+        ffd.ffd_quantize_kv_thumb(k, k2, k2s, kr, krs, begin, seq, cap)
+        qb1.record()
         torch.cuda.synchronize()
+        quant_build_us = qb0.elapsed_time(qb1) * 1e3
 
     Q = args.queries
     if Q > 1 and args.storage == "thumb":
