@@ -13,6 +13,10 @@ Recipe (every workload):
   ``bias="hot"`` picks ``n_hot`` distinct blocks (fixed count, or
   ``max(1, round(hot_frac * NB_b))``) with ``amp ~ U[alpha]``;
   ``bias="lognormal"`` biases every block with ``amp = 0.5 * lognormal(0, 1)``.
+* ``qk_sigma`` scales the draws of q and K (q, K ~ N(0, qk_sigma^2); V stays
+  N(0, 1)); ``k_outlier = (c, a)`` adds ``a * qk_sigma`` to key channel ``c``
+  of every token (one outlier channel). Both are applied to the fp32 draws
+  before the block bias.
 * Values are fp32 draws rounded to bf16 (round half to even).
 * The cache has ``cap = max_b L_b`` rounded up to the block size; rows past
   ``L_b`` are zero, or quiet-NaN when ``poison_tail`` is set (tests use that
@@ -73,6 +77,8 @@ class Workload:
     local: int = 4
     split_blocks: int = 32
     cap: Optional[int] = None                       # cache capacity; default max len rounded up
+    qk_sigma: float = 1.0                           # standard deviation of q and K
+    k_outlier: Optional[Tuple[int, float]] = None   # (channel, amplitude in units of qk_sigma)
 
     @property
     def G(self) -> int:
@@ -126,6 +132,8 @@ def make_inputs(w: Workload, poison_tail: bool = False, threads: Optional[int] =
     else:
         raise ValueError("workload needs lens or len_range")
     q32 = g0.standard_normal((w.B, w.Hq, w.d), dtype=np.float32)
+    if w.qk_sigma != 1.0:
+        q32 = q32 * np.float32(w.qk_sigma)
     q = bf16_bits_from_f32(q32)
 
     bs = w.block_size
@@ -144,6 +152,10 @@ def make_inputs(w: Workload, poison_tail: bool = False, threads: Optional[int] =
         g = np.random.Generator(np.random.PCG64(children[1 + bj]))
         K = g.standard_normal((L, w.d), dtype=np.float32)
         V = g.standard_normal((L, w.d), dtype=np.float32)
+        if w.qk_sigma != 1.0:
+            K *= np.float32(w.qk_sigma)
+        if w.k_outlier is not None:
+            K[:, w.k_outlier[0]] += np.float32(w.k_outlier[1] * w.qk_sigma)
         nb = -(-L // bs)
         if w.bias == "hot" and nb > 0:
             n_hot = w.n_hot if w.n_hot is not None else max(1, int(round(w.hot_frac * nb)))
@@ -187,12 +199,13 @@ def make_inputs(w: Workload, poison_tail: bool = False, threads: Optional[int] =
 
 def make_random_inputs(B: int, Hq: int, Hkv: int, d: int, lens, seed: int, block_size: int = 64,
                        hot_frac: float = 0.05, alpha=(2.0, 4.0), poison_tail: bool = True,
-                       cap: Optional[int] = None) -> dict:
+                       cap: Optional[int] = None, qk_sigma: float = 1.0,
+                       k_outlier: Optional[Tuple[int, float]] = None) -> dict:
     """Small seeded inputs with arbitrary shapes (test helper)."""
     w = Workload(name="random", seed=seed, B=B, Hq=Hq, Hkv=Hkv, d=d,
                  lens=tuple(int(x) for x in lens), block_size=block_size,
                  bias="hot" if hot_frac > 0 else "none", hot_frac=hot_frac, alpha=tuple(alpha),
-                 cap=cap)
+                 cap=cap, qk_sigma=qk_sigma, k_outlier=k_outlier)
     return make_inputs(w, poison_tail=poison_tail)
 
 

@@ -35,19 +35,55 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ``libffd.so``; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+# ffd_decode.hip holds every decode kernel family; it is compiled once per
+# (head dim, dense, key storage) family so that the families build in parallel.
+DECODE_FAMILIES = [(d, dense, thumb) for d in (128, 64) for dense in (0, 1) for thumb in (0, 1)]
+
+
+def _units():
+    """(source, extra defines, object name) of every compilation unit."""
+    units = [(s, [], s.replace(".hip", ".o")) for s in SOURCES if s != "ffd_decode.hip"]
+    for d, dense, thumb in DECODE_FAMILIES:
+        units.append(("ffd_decode.hip",
+                      [f"-DFFD_VARIANT_D={d}", f"-DFFD_VARIANT_DENSE={'true' if dense else 'false'}",
+                       f"-DFFD_VARIANT_THUMB={'true' if thumb else 'false'}"],
+                      f"ffd_decode_d{d}_{'dense' if dense else 'sparse'}_{'thumb' if thumb else 'int4'}.o"))
+    return units
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source into ``libffd.so`` (units in parallel); returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+    def compile_unit(u):
+        src, defs, obj = u
+        cmd = [hipcc(), *flags, *inc, *defs, "-c", os.path.join(CSRC, src), "-o", os.path.join(objdir, obj)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        return cmd, subprocess.run(cmd, capture_output=True, text=True)
+
+    units = _units()
+    jobs = jobs or min(len(units), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(compile_unit, units))
+    for cmd, res in results:
+        if res.returncode != 0:
+            sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed building libffd.so")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC",
+            *[os.path.join(objdir, u[2]) for u in units], "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libffd.so")
-    if verbose and res.stderr.strip():
-        sys.stderr.write(res.stderr)
+        raise RuntimeError("hipcc failed linking libffd.so")
     os.replace(tmp, LIB)
     return LIB
 

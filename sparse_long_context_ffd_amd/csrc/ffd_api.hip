@@ -9,6 +9,26 @@
 #include "ffd.h"
 #include "ffd_internal.h"
 
+namespace ffd {
+
+hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream, bool thumb) {
+  if (D == 128) {
+    if (thumb) return dense ? launch_variant<128, true, true>(p, G, stage, stream)
+                            : launch_variant<128, false, true>(p, G, stage, stream);
+    return dense ? launch_variant<128, true, false>(p, G, stage, stream)
+                 : launch_variant<128, false, false>(p, G, stage, stream);
+  }
+  if (D == 64) {
+    if (thumb) return dense ? launch_variant<64, true, true>(p, G, stage, stream)
+                            : launch_variant<64, false, true>(p, G, stage, stream);
+    return dense ? launch_variant<64, true, false>(p, G, stage, stream)
+                 : launch_variant<64, false, false>(p, G, stage, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ffd
+
 namespace {
 
 thread_local std::string g_err;

@@ -404,9 +404,21 @@ __device__ __forceinline__ bf16x4_t lds_read_tr(const char* p) {
 template <int D>
 struct AttendState {
   f32x4_t o[D / 16];
-  float m;   // running max (base-2 logits), same in the 4 lanes of a head
-  float l;   // this lane's share of the normaliser
+  float m;      // running max (base-2 logits), same in the 4 lanes of a head
+  float l;      // this lane's share of the normaliser
+  bool fresh;   // the row has met no exact logit yet (o and l are still 0)
 };
+
+// How far (base-2 logit units) the scan's seed may sit above the first exact
+// block maximum of a row before it is replaced by that maximum. The low-bit
+// score of a token can overshoot its exact logit by far more than the
+// exponent range of fp32 (a coarse sketch, large logits, an outlier key
+// channel); a seed kept that high would flush every weight exp2(z - m) to 0.
+// While a row is fresh nothing has been accumulated relative to m, so moving
+// m down is exact; afterwards m stays within this slack of the largest exact
+// logit the row has met, so its largest weight is >= 2^-64 and the smallest
+// nonzero weights it drops are below 2^-62 of the row's sum.
+constexpr float kSeedSlack = 64.f;
 
 // Lrow: tokens this lane's row (lane % 16) may see; L: tokens of the sequence
 // (the longest row), which bounds every load.
@@ -455,6 +467,7 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   for (int nt = 0; nt < NT; ++nt) st.o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   st.m = hv ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
   st.l = 0.f;
+  st.fresh = true;
 
   char* vt = reinterpret_cast<char*>(sm.vt[w]);
   // LDS addresses of the V tile. Store: 16-byte chunk n*64 + lane of the tile
@@ -611,10 +624,14 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool up = mx > st.m;
+    // a fresh row takes the block's exact max when the seed lies too far
+    // above it (nothing to rescale: o and l are 0); afterwards m only rises
+    const bool fresh = st.fresh;
+    const bool up = mx > st.m || (!DENSE && fresh && mx != -INFINITY && mx < st.m - kSeedSlack);
+    if (mx != -INFINITY) st.fresh = false;
     if (__ballot(up)) {
       const float mn = up ? mx : st.m;
-      const float alpha = (st.m == -INFINITY) ? 0.f : fast_exp2(st.m - mn);
+      const float alpha = (st.m == -INFINITY || fresh) ? 0.f : fast_exp2(st.m - mn);
       st.m = mn;
       st.l *= alpha;
 #pragma unroll
@@ -844,13 +861,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // per row, once: the waves' weights exp2(m_w - m) / den and the LSE
   if (tid < R) {
     const int h = tid;
+    // a wave that accumulated nothing for the row (its m may still be the
+    // seed, above every exact logit) takes no part in the merge
+    float wmv[NW];
     float mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sm.wm[ww][h]);
+    for (int ww = 0; ww < NW; ++ww) {
+      wmv[ww] = sm.wl[ww][h] > 0.f ? sm.wm[ww][h] : -INFINITY;
+      mx = fmaxf(mx, wmv[ww]);
+    }
     float a[NW], den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      a[ww] = (sm.wm[ww][h] == -INFINITY) ? 0.f : exp2f(sm.wm[ww][h] - mx);
+      a[ww] = (wmv[ww] == -INFINITY) ? 0.f : exp2f(wmv[ww] - mx);
       den += sm.wl[ww][h] * a[ww];
     }
     // a row can keep no block of a split (sink/local pseudo-max, or a query
@@ -1028,20 +1051,30 @@ hipError_t launch_g(const DecodeParams& p, int G, Stage stage, hipStream_t strea
   }
 }
 
-template <int D, bool THUMB>
-hipError_t launch_dt(const DecodeParams& p, int G, bool dense, Stage stage, hipStream_t stream) {
-  return dense ? launch_g<D, true, THUMB>(p, G, stage, stream) : launch_g<D, false, THUMB>(p, G, stage, stream);
-}
-
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream,
-                         bool thumb) {
-  if (D == 128) return thumb ? launch_dt<128, true>(p, G, dense, stage, stream)
-                             : launch_dt<128, false>(p, G, dense, stage, stream);
-  if (D == 64) return thumb ? launch_dt<64, true>(p, G, dense, stage, stream)
-                            : launch_dt<64, false>(p, G, dense, stage, stream);
-  return hipErrorInvalidValue;
+// One family of kernels (head dim D, dense or sparse, key storage) per
+// compilation of this file: the build compiles it once per family with
+// FFD_VARIANT_D, FFD_VARIANT_DENSE and FFD_VARIANT_THUMB defined, so the
+// families compile in parallel; with none defined every family is
+// instantiated here.
+template <int D, bool DENSE, bool THUMB>
+hipError_t launch_variant(const DecodeParams& p, int G, Stage stage, hipStream_t stream) {
+  return launch_g<D, DENSE, THUMB>(p, G, stage, stream);
 }
+
+#if defined(FFD_VARIANT_D)
+template hipError_t launch_variant<FFD_VARIANT_D, FFD_VARIANT_DENSE, FFD_VARIANT_THUMB>(const DecodeParams&, int, Stage,
+                                                                                      hipStream_t);
+#else
+template hipError_t launch_variant<128, false, false>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<128, true, false>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<128, false, true>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<128, true, true>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<64, false, false>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<64, true, false>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<64, false, true>(const DecodeParams&, int, Stage, hipStream_t);
+template hipError_t launch_variant<64, true, true>(const DecodeParams&, int, Stage, hipStream_t);
+#endif
 
 }  // namespace ffd

@@ -90,9 +90,16 @@ hipError_t launch_quantize_thumb(const uint16_t* k, uint8_t* k2, float* k2scale,
 
 enum class Stage { kPartials = 1, kCombine = 2, kBoth = 3 };
 
-// Returns hipErrorInvalidValue for an unsupported (D, G, p.Q) combination
-// (G * Q <= 16; Q > 1 only with the int4 storage). thumb: K comes from the
+// The kernels of one (D, dense, thumb) family (defined in ffd_decode.hip).
+// Returns hipErrorInvalidValue for an unsupported (G, p.Q) combination
+// (G * Q <= 16; Q > 1 only with the int4 storage). THUMB: K comes from the
 // thumbnail + residual storage instead of bf16 K and the int4 sketch.
+template <int D, bool DENSE, bool THUMB>
+hipError_t launch_variant(const DecodeParams& p, int G, Stage stage, hipStream_t stream);
+
+// Dispatch on the runtime (D, dense, thumb) (defined in ffd_api.hip, outside
+// the translation units that define the kernel families);
+// hipErrorInvalidValue for an unsupported combination.
 hipError_t launch_decode(const DecodeParams& p, int D, int G, bool dense, Stage stage, hipStream_t stream,
                          bool thumb = false);
 

@@ -14,6 +14,7 @@ import torch
 import sparse_long_context_ffd_amd as ffd
 from ffd_inputs import WORKLOADS, make_inputs, make_random_inputs, multi_query
 from oracle import ffd_oracle as O
+from tests import oracle_par as P
 from tests.gpu_util import assert_close, assert_mask_equal, dev_bf16, say, sm_scale_for, to_device
 
 pytestmark = pytest.mark.gpu
@@ -103,8 +104,8 @@ def test_deterministic():
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("name,Q,full", [("llama3_8b_32k", 4, True), ("llama3_8b_128k_b4", 4, False)])
-def test_workload(name, Q, full):
+@pytest.mark.parametrize("name,Q", [("llama3_8b_32k", 4), ("llama3_8b_128k_b4", 4)])
+def test_workload(name, Q):
     w = WORKLOADS[name]
     say(f"multi-query workload {name} Q={Q}: generating")
     inp = make_inputs(w)
@@ -118,21 +119,11 @@ def test_workload(name, Q, full):
                           split_blocks=w.split_blocks, sm_scale=sm, kq=kq, ks=ks)
     args = dict(max_seq_len=inp["cap"], block_size=64, delta=delta, sink=w.sink, local=w.local,
                 split_blocks=w.split_blocks, sm_scale=np.float32(sm))
-    if full:
-        say("  oracle (all rows)")
-        r_out, r_lse, r_mask = O.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], **args)
-        assert_mask_equal(mask, r_mask, f"{name} mask")
-        assert_close(out, r_out, f"{name} out")
-        assert_close(lse, r_lse, f"{name} lse")
-    else:
-        rng = np.random.default_rng(7)
-        rows = sorted({(int(rng.integers(w.B)), int(rng.integers(Q)), int(rng.integers(w.Hq))) for _ in range(6)})
-        say(f"  oracle on rows {rows}")
-        r_out, r_lse, r_mask = O.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], heads=rows, **args)
-        for b, i, h in rows:
-            assert_mask_equal(mask[b, i, h], r_mask[b, i, h], f"{name} mask {(b, i, h)}")
-            assert_close(out[b, i, h], r_out[b, i, h], f"{name} out {(b, i, h)}")
-            assert_close(lse[b, i, h], r_lse[b, i, h], f"{name} lse {(b, i, h)}")
+    say("  oracle (every row)")
+    r_out, r_lse, r_mask = P.decode_multi(qm, inp["k"], inp["v"], inp["seq_lens"], **args)
+    assert_mask_equal(mask, r_mask, f"{name} mask")
+    assert_close(out, r_out, f"{name} out")
+    assert_close(lse, r_lse, f"{name} lse")
 
 
 def test_negative_lengths_are_empty():
