@@ -11,7 +11,8 @@
  * Conventions shared by every entry point:
  *   - Every tensor argument is a DEVICE pointer to contiguous row-major
  *     memory that the caller allocated and owns. The library allocates
- *     nothing, keeps no state except a per-thread error string, and never
+ *     nothing, keeps no state except a per-thread error string (and the
+ *     static scratch array of ffd_decode_noalloc, one per device), and never
  *     synchronises: work is enqueued on `stream` (a hipStream_t; NULL means
  *     the default stream) and the call returns at once.
  *   - bf16 tensors hold IEEE bfloat16 values (raw 16-bit patterns).
@@ -339,6 +340,32 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
                        int block_size, int split_blocks, const void* workspace,
                        size_t workspace_bytes, void* out, int out_dtype, float* lse,
                        void* stream);
+
+/*
+ * ffd_decode_noalloc -- ffd_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments as ffd_decode minus the workspace; same
+ * kernels, semantics and results. The per-split partials go to a static
+ * device array of FFD_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it is loaded on until the process ends; the call allocates nothing.
+ *   - Sizes whose partials need more (ffd_decode_workspace_bytes above
+ *     FFD_NOALLOC_SCRATCH_BYTES) give FFD_ERR_WORKSPACE and enqueue nothing.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's partials (nothing in it needs clearing). Calls that overlap
+ *     on one device -- on different streams with no ordering between them --
+ *     race on it and give wrong results; calls on one stream never overlap.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress, no allocation); make that first call outside
+ *     stream capture.
+ */
+#define FFD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+ffd_status ffd_decode_noalloc(const void* q, const void* k, const void* v,
+                              const uint8_t* kq, const float* kscale, const int32_t* seq_lens,
+                              int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
+                              int block_size, float delta, int sink_blocks, int local_blocks,
+                              int pseudo_max, int split_blocks, float sm_scale,
+                              void* out, int out_dtype, float* lse, uint8_t* kept_mask, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ from .ffd import (  # noqa: F401
     FFD_OK,
     FFDError,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     alloc_workspace,
     decode,
     decode_multi,
@@ -23,6 +24,7 @@ from .ffd import (  # noqa: F401
     ffd_decode,
     ffd_decode_multi,
     ffd_decode_multi_workspace_bytes,
+    ffd_decode_noalloc,
     ffd_decode_paged,
     ffd_decode_paged_multi,
     ffd_decode_partials,

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "ffd.h"
@@ -517,6 +518,90 @@ ffd_status ffd_combine(const int32_t* seq_lens, int max_seq_len, int B, int Hq, 
   p.waves = ns > 0 ? ffd::waves_for(B, Hq, ns) : 4;
   p.split_blocks = split_blocks;
   return launch(fn, p, d, 1, false, ffd::Stage::kCombine, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// ffd_decode_noalloc: ffd_decode with the split partials in a static device
+// array instead of a caller workspace.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = FFD_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+// The partials of ffd_decode_noalloc. Every device the library's code object
+// is loaded on holds its own copy until the process ends. In host code this
+// name is a host-side stand-in, not a device address: kernels get the address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // per device, looked up on its first call
+
+ffd_status scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FFD_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FFD_ERR_UNSUPPORTED, "%s: device %d outside the %d devices the scratch table holds", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(FFD_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FFD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ffd_status ffd_decode_noalloc(const void* q, const void* k, const void* v, const uint8_t* kq, const float* kscale,
+                              const int32_t* seq_lens, int max_seq_len, int B, int Hq, int Hkv, int d, int cap,
+                              int block_size, float delta, int sink_blocks, int local_blocks, int pseudo_max,
+                              int split_blocks, float sm_scale, void* out, int out_dtype, float* lse,
+                              uint8_t* kept_mask, void* stream) {
+  const char* fn = "ffd_decode_noalloc";
+  ffd_status st = check_out_dtype(fn, out_dtype);
+  if (st != FFD_OK) return st;
+  const size_t need = ffd_decode_workspace_bytes(B, Hq, d, max_seq_len, block_size, split_blocks);
+  if (need > kScratchBytes)
+    return fail(FFD_ERR_WORKSPACE,
+                "%s: these sizes need %zu bytes of partials, above the %zu bytes of the static scratch array "
+                "(use ffd_decode with a workspace)",
+                fn, need, kScratchBytes);
+  // Validate everything on the host first, against a stand-in workspace
+  // address (aligned, never dereferenced), then carve the real array.
+  char* const stand_in = reinterpret_cast<char*>(ffd::kWsAlign);
+  ffd::DecodeParams p;
+  int G;
+  bool dense;
+  st = prepare_decode(fn, q, k, v, kq, kscale, seq_lens, max_seq_len, B, 1, Hq, Hkv, d, cap, block_size, delta,
+                      sink_blocks, local_blocks, pseudo_max, split_blocks, sm_scale, kept_mask, stand_in,
+                      kScratchBytes, nullptr, 0, 0, p, G, dense);
+  if (st != FFD_OK) return st;
+  st = check_out_ptrs(fn, B, out, lse);
+  if (st != FFD_OK) return st;
+  if (p.o_part != nullptr) {
+    void* base = nullptr;
+    st = scratch_for_current_device(fn, &base);
+    if (st != FFD_OK) return st;
+    char* ws = static_cast<char*>(base);
+    p.lse_part = reinterpret_cast<float*>(ws + (reinterpret_cast<char*>(p.lse_part) - stand_in));
+    p.o_part = reinterpret_cast<float*>(ws);
+  }
+  p.out = out;
+  p.lse = lse;
+  p.out_f32 = out_dtype == FFD_OUT_F32;
+  return launch(fn, p, d, G, dense, ffd::Stage::kBoth, stream);
 }
 
 }  // extern "C"

@@ -10,7 +10,8 @@ the int4 sketch ``ffd_quantize_kv`` / ``ffd_decode`` and its halves
 ``ffd_decode_partials`` / ``ffd_combine``, the thumbnail storage
 ``ffd_quantize_kv_thumb`` / ``ffd_decode_thumb``, the paged cache
 ``ffd_quantize_kv_paged`` / ``ffd_decode_paged``, several query tokens
-``ffd_decode_multi`` / ``ffd_decode_paged_multi``, the workspace sizes, ``ffd_last_error`` and
+``ffd_decode_multi`` / ``ffd_decode_paged_multi``, ``ffd_decode_noalloc``
+(no workspace: a static device array), the workspace sizes, ``ffd_last_error`` and
 ``ffd_abi_version``) and take preallocated tensors. ``quantize_kv``,
 ``quantize_kv_thumb``, ``decode`` and ``decode_multi`` are conveniences that
 allocate the outputs and the workspace with torch and then call them.
@@ -39,7 +40,8 @@ PSEUDO_MAX = {"split": 0, "sink_local": 1, "max": 2}
 EXPORTED_SYMBOLS = ("ffd_abi_version", "ffd_last_error", "ffd_quantize_kv", "ffd_quantize_kv_paged",
                     "ffd_quantize_kv_thumb", "ffd_decode_workspace_bytes", "ffd_decode", "ffd_decode_paged",
                     "ffd_decode_thumb", "ffd_decode_partials", "ffd_combine", "ffd_decode_multi",
-                    "ffd_decode_multi_workspace_bytes", "ffd_decode_paged_multi")
+                    "ffd_decode_multi_workspace_bytes", "ffd_decode_paged_multi", "ffd_decode_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20   # FFD_NOALLOC_SCRATCH_BYTES
 
 
 class FFDError(RuntimeError):
@@ -113,6 +115,12 @@ def lib() -> ctypes.CDLL:
                                    _i, ctypes.c_float, _i, _i, _i, _i,         # block_size delta sink local pm split
                                    ctypes.c_float, _vp, _i, _vp, _vp,          # sm_scale out out_dtype lse mask
                                    _vp, ctypes.c_size_t, _vp]                  # workspace bytes stream
+    L.ffd_decode_noalloc.restype = _i
+    L.ffd_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp,          # q k v kq kscale seq_lens
+                                     _i, _i, _i, _i, _i, _i,                # max_seq_len B Hq Hkv d cap
+                                     _i, ctypes.c_float, _i, _i, _i, _i,    # block_size delta sink local pm split
+                                     ctypes.c_float,                        # sm_scale
+                                     _vp, _i, _vp, _vp, _vp]                # out out_dtype lse mask stream
     L.ffd_combine.restype = _i
     L.ffd_combine.argtypes = [_vp, _i, _i, _i, _i, _i, _i, _vp, ctypes.c_size_t, _vp, _i, _vp, _vp]
     _lib = L
@@ -233,6 +241,21 @@ def ffd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[t
                             int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out), odt,
                             _ptr(lse),
                             _ptr(kept_mask), _ptr(workspace), _ws(workspace), _stream(stream)))
+
+
+def ffd_decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kq: Optional[torch.Tensor],
+                       kscale: Optional[torch.Tensor], seq_lens: torch.Tensor, *, max_seq_len: int,
+                       block_size: int, delta: float, sink: int, local: int, split_blocks: int, sm_scale: float,
+                       out: torch.Tensor, lse: torch.Tensor, kept_mask: Optional[torch.Tensor],
+                       pseudo_max: str = "split", stream=None) -> None:
+    """``ffd_decode`` with the partials in the library's static scratch array
+    (no workspace argument, no allocation)."""
+    B, Hq, Hkv, d, cap = _check_decode_inputs(q, k, v, kq, kscale, seq_lens, max_seq_len, block_size, kept_mask)
+    odt = _check_outputs(out, lse, B, Hq, d)
+    _check(lib().ffd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kq), _ptr(kscale), _ptr(seq_lens),
+                                    int(max_seq_len), B, Hq, Hkv, d, cap, int(block_size), float(delta), int(sink),
+                                    int(local), _pm(pseudo_max), int(split_blocks), float(sm_scale), _ptr(out),
+                                    odt, _ptr(lse), _ptr(kept_mask), _stream(stream)))
 
 
 def ffd_decode_multi_workspace_bytes(B: int, Q: int, Hq: int, d: int, max_seq_len: int, block_size: int = 64,

@@ -231,3 +231,35 @@ def test_token_counts_above_2_30_are_rejected_not_overflowed():
     assert L.ffd_quantize_kv_paged(fake, fake, fake, fake, 2 ** 25, 4, fake, fake, 1, 8, 128, 16,
                                    None) == ffd.FFD_ERR_UNSUPPORTED
     assert L.ffd_combine(fake, big, 1, 32, 128, 64, 32, fake, 1 << 40, fake, 0, fake, None) == ffd.FFD_ERR_UNSUPPORTED
+
+
+def _noalloc(**kw):
+    """ffd_decode_noalloc with stand-in (never dereferenced) device pointers."""
+    fake = ctypes.c_void_p(1 << 20)
+    args = dict(max_seq_len=128, B=1, Hq=4, Hkv=1, d=128, cap=128, block_size=64, delta=6.0, pm=0, split=32)
+    args.update(kw)
+    return ffd.lib().ffd_decode_noalloc(fake, fake, fake, fake, fake, fake, args["max_seq_len"], args["B"],
+                                        args["Hq"], args["Hkv"], args["d"], args["cap"], args["block_size"],
+                                        ctypes.c_float(args["delta"]), 1, 4, args["pm"], args["split"],
+                                        ctypes.c_float(0.088388), fake, 0, fake, None, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(B=8, Hq=64, max_seq_len=1 << 20, cap=1 << 20, split=16), ffd.FFD_ERR_WORKSPACE, "static scratch"),
+    (dict(Hq=6, Hkv=4), ffd.FFD_ERR_INVALID_ARG, "multiple"),
+    (dict(split=0), ffd.FFD_ERR_INVALID_ARG, "split_blocks"),
+    (dict(d=96), ffd.FFD_ERR_UNSUPPORTED, "d=96"),
+    (dict(cap=64), ffd.FFD_ERR_INVALID_ARG, "cap"),
+])
+def test_noalloc_rejects_on_host(kw, status, needle):
+    """Sizes beyond the static array and bad arguments are refused before any
+    device call (these run without a GPU)."""
+    assert _noalloc(**kw) == status
+    assert needle in ffd.ffd_last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    with open(os.path.join(ROOT, "include", "ffd.h")) as f:
+        src = f.read()
+    m = re.search(r"#define FFD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ffd.NOALLOC_SCRATCH_BYTES
