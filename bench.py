@@ -182,8 +182,25 @@ def main() -> int:
     ap.add_argument("--split-blocks", type=int, default=None,
                     help="blocks per split (the split whose max sets the Top-delta threshold); default: the workload's")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="only run a plain 1 GiB read+write elementwise kernel (counter calibration)")
+                    help="only run a plain 1 GiB read+write elementwise kernel (checks the byte counters)")
+    ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
+                    help="before every timed step, outside the timed region: read (default) or write a 512 MiB "
+                         "scratch buffer so that the step finds nothing of its inputs in the L2s or the MALL; "
+                         "'none' times the steps back to back")
+    ap.add_argument("--profile-summary", metavar="OUT_STEM", default=None,
+                    help="no GPU work: turn rocprofv3 CSV output (--trace-dir, --pmc-dirs, --copy-pmc-dirs) and "
+                         "the JSON line of the profiled bench run (--bench-json) into profiles/OUT_STEM_*")
+    ap.add_argument("--trace-dir", default=None)
+    ap.add_argument("--pmc-dirs", default="", help="comma-separated rocprofv3 --pmc output directories")
+    ap.add_argument("--copy-pmc-dirs", default="", help="the same counters on --copy-probe")
+    ap.add_argument("--bench-json", default=None, help="file holding the profiled run's JSON line")
+    ap.add_argument("--commands", default="", help="file holding the commands that made the profiles")
     args = ap.parse_args()
+
+    if args.profile_summary:
+        from bench_profiles import write_summaries
+
+        return write_summaries(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -212,6 +229,20 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n, "launches": 5}))
         return 0
+
+    # cache flush between timed steps: 512 MiB, twice the 256 MB MALL and far
+    # above the eight 4 MB L2s. A read leaves the caches holding clean scratch
+    # lines; a write leaves them dirty, and their write-back then lands inside
+    # the next timed step.
+    flush_elems = (512 << 20) // 4
+    scratch = torch.ones(flush_elems, dtype=torch.float32, device=dev) if args.flush != "none" else None
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        if args.flush == "read":
+            torch.sum(scratch, dim=0, out=flush_sink)
+        elif args.flush == "write":
+            scratch.fill_(1.0)
 
     w = WORKLOADS[args.workload]
     if args.split_blocks is not None:
@@ -347,40 +378,51 @@ def main() -> int:
             ev[2].record()
 
     def timed(dl, steps, warmup):
-        """Eager steps with HIP events around each launch (per-kernel times),
-        then -- unless --no-graph -- the same step captured once in a HIP graph
-        and replayed (the step's wall time without host launch gaps, as a
-        serving loop would issue it). Returns (wall per step in s, eager wall
-        per step in s, fused us[], combine us[])."""
+        """Per-step timing with HIP events on the launch stream, a cache flush
+        before every step outside the events. First eager launches with
+        events around each kernel (per-kernel durations for the roofline),
+        then -- unless --no-graph -- the same step captured once in a HIP
+        graph and replayed (the step as a serving loop issues it, without host
+        launch gaps). Returns (step us[], eager step us[], fused us[],
+        combine us[], back-to-back wall per step in s)."""
         for _ in range(warmup):
             step(dl)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
-        t_a = time.perf_counter()
         for i in range(steps):
+            flush()
             step(dl, evs[i])
         torch.cuda.synchronize()
-        wall_eager = (time.perf_counter() - t_a) / steps
         fused = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in evs])
         comb = np.array([e[1].elapsed_time(e[2]) * 1e3 for e in evs])
+        eager = np.array([e[0].elapsed_time(e[2]) * 1e3 for e in evs])
         if args.no_graph:
-            return wall_eager, wall_eager, fused, comb
+            return eager, eager, fused, comb, None
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             step(dl)
         for _ in range(warmup):
             g.replay()
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
+        for i in range(steps):
+            flush()
+            sev[i][0].record()
+            g.replay()
+            sev[i][1].record()
+        torch.cuda.synchronize()
+        step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in sev])
+        # the old back-to-back figure, for comparison: K replays, no flush
         t_a = time.perf_counter()
         for _ in range(steps):
             g.replay()
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t_a) / steps
+        b2b = (time.perf_counter() - t_a) / steps
         del g
-        return wall, wall_eager, fused, comb
+        return step_us, eager, fused, comb, b2b
 
-    wall, wall_eager, fused_us, comb_us = timed(delta, args.steps, args.warmup)
-    step_us_wall = wall * 1e6
+    step_us_all, eager_us, fused_us, comb_us, b2b = timed(delta, args.steps, args.warmup)
+    step_us_med = float(np.median(step_us_all))
     m = mask.cpu().numpy()
     if Q > 1:
         m_rows = m
@@ -393,7 +435,7 @@ def main() -> int:
         head_keep = float(m_rows.sum() / max(1, vis * w.Hq))
     fused_avg = float(fused_us.mean())
     achieved = alg_bytes / (fused_avg * 1e-6) / 1e9
-    value = alg_bytes / (step_us_wall * 1e-6) / 1e9
+    value = alg_bytes / (step_us_med * 1e-6) / 1e9
 
     # counter summaries are taken in the default split size, one query token
     traffic = None
@@ -407,8 +449,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_us_wall / 1e3, 4),
-        "us_per_step": round(step_us_wall, 2),
+        "ms_per_step": round(step_us_med / 1e3, 4),
+        "us_per_step": round(step_us_med, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -421,6 +463,7 @@ def main() -> int:
             "split_blocks": w.split_blocks, "pseudo_max": args.pseudo_max, "out_dtype": "f32",
             "kv_layout": "paged (64-token pages, shuffled)" if args.paged else "contiguous",
             "query_tokens": Q,
+            "diagnostic": w.diagnostic or None,
             "key_storage": ("2-bit thumbnail + int8 residual (K^ refinement)" if args.storage == "thumb"
                             else "int4 sketch + bf16 K"),
         },
@@ -441,13 +484,21 @@ def main() -> int:
             "avg_launch_us": round(fused_avg, 2),
         },
         "timing_us": {
+            "step_median": round(step_us_med, 2),
+            "step_p10": round(float(np.percentile(step_us_all, 10)), 2),
+            "step_p90": round(float(np.percentile(step_us_all, 90)), 2),
+            "step_mean": round(float(step_us_all.mean()), 2),
+            "step_timing": ("eager launches" if args.no_graph else "replays of the step captured in a HIP graph")
+                           + ", HIP events on the launch stream around each step",
+            "flush": ("none (steps back to back)" if args.flush == "none" else
+                      f"512 MiB scratch {args.flush} before every timed step, outside the events"),
+            "step_eager_median": round(float(np.median(eager_us)), 2),
+            "fused_mean": round(fused_avg, 2),
             "fused_median": round(float(np.median(fused_us)), 2),
             "fused_p10": round(float(np.percentile(fused_us, 10)), 2),
             "fused_p90": round(float(np.percentile(fused_us, 90)), 2),
             "combine_median": round(float(np.median(comb_us)), 2),
-            "step_wall": round(step_us_wall, 2),
-            "step_wall_eager": round(wall_eager * 1e6, 2),
-            "step_timing": "eager launches" if args.no_graph else "replays of the step captured in a HIP graph",
+            "step_back_to_back_no_flush": None if b2b is None else round(b2b * 1e6, 2),
             "quantize_build": round(quant_build_us, 1),
         },
         "bytes": {"scan": int(scan_b), "kv": int(kv_b)},
@@ -457,13 +508,13 @@ def main() -> int:
     }
 
     if not args.no_dense and not dense:
-        wall_d, _, fused_d, _ = timed(math.inf, max(10, args.steps // 5), 3)
+        step_d, _, fused_d, _, _ = timed(math.inf, max(10, args.steps // 5), 3)
         md = mask.cpu().numpy()
         if Q > 1:
             md = md.max(axis=1)
         _, kv_d, _ = algorithmic_bytes(md, inp["seq_lens"], Hkv, G, d, w.block_size, True, args.storage)
         rec["dense_delta_inf"] = {
-            "us_per_step": round(wall_d * 1e6, 2),
+            "us_per_step": round(float(np.median(step_d)), 2),
             "fused_median_us": round(float(np.median(fused_d)), 2),
             "fused_GBps": round(kv_d / (float(fused_d.mean()) * 1e-6) / 1e9, 1),
             "sparse_speedup": round(float(np.median(fused_d)) / float(np.median(fused_us)), 3),

@@ -79,6 +79,7 @@ class Workload:
     cap: Optional[int] = None                       # cache capacity; default max len rounded up
     qk_sigma: float = 1.0                           # standard deviation of q and K
     k_outlier: Optional[Tuple[int, float]] = None   # (channel, amplitude in units of qk_sigma)
+    diagnostic: str = ""                            # non-empty: not a headline workload; says what it is for
 
     @property
     def G(self) -> int:
@@ -101,6 +102,14 @@ WORKLOADS = {
     "mixed_16x8k_128k": Workload(
         name="mixed_16x8k_128k", seed=5, B=16, Hq=32, Hkv=8, d=128, len_range=(8192, 131072),
         bias="lognormal", deltas=(6.0,), sink=1, local=4),
+    # Diagnostic: the 256K head shape with peaked attention (2% of blocks
+    # pushed hard toward the group's query), so that Top-δ drops a large,
+    # uneven share of the blocks (per split from 1 to all 32 kept); it shows
+    # whether time follows the bytes actually read.
+    "diag_256k_peaked": Workload(
+        name="diag_256k_peaked", seed=6, B=1, Hq=32, Hkv=8, d=128, lens=(262144,),
+        hot_frac=0.02, alpha=(6.0, 10.0), deltas=(2.0, 1.0, 4.0, math.inf), sink=1, local=4,
+        diagnostic="peaked attention for the skip path (uneven kept counts per split); not a headline workload"),
 }
 
 
