@@ -166,17 +166,29 @@ __device__ __forceinline__ int scan_rotation(const DecodeParams& p, int j0, int 
   return (p.block_table != nullptr && nblk > 0) ? (j0 / p.split_blocks) % nblk : 0;
 }
 
+// Per-lane constants of the scan: the B operand (the int8 query rows in the
+// order the codes unpack), the offset-binary correction, cq and the row's
+// visible length. Lane (g, n) serves row n (rows past R: no tokens).
+template <int D, bool THUMB>
+struct ScanQuery {
+  i32x4_t qa[D / 64];
+  i32x4_t acc0;
+  int corr;
+  float cq;
+  int Lr;     // tokens row n sees
+  int Lmin;   // tokens the first query token's rows see (the fewest)
+};
+
 template <int D, int G, int QT, bool THUMB, int NW>
-__device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
-                                               int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
+__device__ __forceinline__ ScanQuery<D, THUMB> scan_query(const DecodeParams& p, const DecodeSmem<D, G * QT, NW>& sm,
+                                                          int sl, int lane) {
   constexpr int R = G * QT;
   constexpr int NM = D / 64;   // MFMAs per tile (k = 64 each)
-  const int nblk = nblk_split + nx;
   const int n = lane & 15;
   const int g = lane >> 4;
+  ScanQuery<D, THUMB> sq;
   // B operand: word e of MFMA s holds dims g*D/4 + 8*(2s + e/2) + 2*i + (e & 1)
   // (int4) or g*D/4 + 16s + 4i + e (thumbnail), i = 0..3, of row n
-  i32x4_t qa[NM];
 #pragma unroll
   for (int s = 0; s < NM; ++s)
 #pragma unroll
@@ -184,18 +196,126 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
       const int8_t* qrow = &sm.qc[n < R ? n : 0][g * (D / 4)];
       if constexpr (THUMB) {
         const int8_t* q8 = qrow + 16 * s + e;
-        qa[s][e] = n < R ? pack4_i8(q8[0], q8[4], q8[8], q8[12]) : 0;
+        sq.qa[s][e] = n < R ? pack4_i8(q8[0], q8[4], q8[8], q8[12]) : 0;
       } else {
         const int8_t* q8 = qrow + 8 * (2 * s + e / 2) + (e & 1);
-        qa[s][e] = n < R ? pack4_i8(q8[0], q8[2], q8[4], q8[6]) : 0;
+        sq.qa[s][e] = n < R ? pack4_i8(q8[0], q8[2], q8[4], q8[6]) : 0;
       }
     }
   // row n's correction, scale and length (rows past R: no tokens)
-  const int corr = n < R ? (THUMB ? 3 : 8) * sm.sumq[n] : 0;
-  const float cq = n < R ? sm.cq[n] : 0.f;
-  const int Lr = n < R ? row_len<G>(p, sl, n) : 0;
-  const int Lmin = row_len<G>(p, sl, 0);   // the first query token's rows see the fewest tokens
-  const i32x4_t acc0 = THUMB ? i32x4_t{0, 0, 0, 0} : i32x4_t{-corr, -corr, -corr, -corr};
+  sq.corr = n < R ? (THUMB ? 3 : 8) * sm.sumq[n] : 0;
+  sq.cq = n < R ? sm.cq[n] : 0.f;
+  sq.Lr = n < R ? row_len<G>(p, sl, n) : 0;
+  sq.Lmin = row_len<G>(p, sl, 0);
+  sq.acc0 = THUMB ? i32x4_t{0, 0, 0, 0} : i32x4_t{-sq.corr, -sq.corr, -sq.corr, -sq.corr};
+  return sq;
+}
+
+// Code bytes per token in the scan's sketch: D/2 (int4) or D/4 (thumbnail).
+template <int D, bool THUMB>
+constexpr int sketch_row_bytes() { return THUMB ? D / 4 : D / 2; }
+
+// Issue the loads of one block's sketch for one wave: lane (g, n) gets the
+// code bytes g*RB/4 .. +RB/4 of token t0 + 16T + n of each tile T, and the
+// scale of token t0 + 16*(n/4) + 4g + n%4; tokens at or past L are not read
+// (zero). The int4 sketch is read once (streaming loads); thumbnail codes and
+// scales use ordinary loads, since a kept block's are used again.
+template <int D, bool THUMB>
+__device__ __forceinline__ void load_sketch(const DecodeParams& p, size_t r0, int t0, int L, int lane, u32x4_t (&cw)[4],
+                                            float& scl) {
+  constexpr int RB = sketch_row_bytes<D, THUMB>();
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const uint8_t* kq = (THUMB ? p.k2 : p.kq) + r0 * RB;
+  const float* ks = (THUMB ? p.k2scale : p.kscale) + r0;
+  // (Loading every row from a clamped address and zeroing the ones past the
+  // sequence afterwards, with no branch around a load, measured 1-4% slower.)
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    const int t = t0 + 16 * T + n;
+    const bool ok = t < L;
+    const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * RB + g * (RB / 4);
+    if constexpr (RB / 4 == 16) {
+      cw[T] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
+    } else if constexpr (RB / 4 == 8) {
+      const u32x2_t* s2 = reinterpret_cast<const u32x2_t*>(src);
+      const u32x2_t u = ok ? (THUMB ? *s2 : __builtin_nontemporal_load(s2)) : u32x2_t{0u, 0u};
+      cw[T] = u32x4_t{u.x, u.y, 0u, 0u};
+    } else {
+      const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
+      const uint32_t u = ok ? (THUMB ? *s1 : __builtin_nontemporal_load(s1)) : 0u;
+      cw[T] = u32x4_t{u, 0u, 0u, 0u};
+    }
+  }
+  // the 16 scales lane (g, n) needs (tokens 16T + 4g + r) are held by
+  // lanes 4T + r of its own 16-lane row: one load per lane, then row
+  // broadcasts; tokens past the sequence are not read
+  const int tl = 16 * (n >> 2) + 4 * g + (n & 3);
+  scl = t0 + tl < L ? (THUMB ? ks[tl] : __builtin_nontemporal_load(ks + tl)) : 0.f;
+}
+
+// score_block with the B operand given by pointer (registers, or LDS where
+// the caller cannot spare the registers).
+template <int D, bool THUMB, typename QA>
+__device__ __forceinline__ float score_block_q(const ScanQuery<D, THUMB>& sq, QA qa, const u32x4_t (&cw)[4], float scl,
+                                               int t0, int lane) {
+  constexpr int NM = D / 64;
+  const int g = lane >> 4;
+  float bm = -INFINITY;
+  // scores of the block's 4 tiles; MASKED: drop the tokens row n cannot see
+  auto tiles = [&](auto masked) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      i32x4_t acc = sq.acc0;
+#pragma unroll
+      for (int s = 0; s < NM; ++s) {
+        i32x4_t kb;
+        if constexpr (THUMB) {
+          const uint32_t x = cw[T][s];
+          kb = i32x4_t{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
+                       (int)((x >> 6) & 0x03030303u)};
+        } else {
+          // two's complement -> code + 8, low and high nibbles
+          const uint32_t x0 = cw[T][2 * s], x1 = cw[T][2 * s + 1];
+          kb = i32x4_t{(int)((x0 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x0 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu),
+                       (int)((x1 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x1 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu)};
+        }
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb, qa[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float wgt = row_bcast_f(scl, 4 * T + r) * sq.cq;
+        const int dot = THUMB ? 2 * acc[r] - sq.corr : acc[r];
+        const float sv = (float)dot * wgt;
+        if constexpr (decltype(masked)::value)
+          bm = fmaxf(bm, t0 + 16 * T + 4 * g + r < sq.Lr ? sv : -INFINITY);
+        else
+          bm = fmaxf(bm, sv);
+      }
+    }
+  };
+  if (t0 + kBlockSize <= sq.Lmin) tiles(std::false_type{});
+  else tiles(std::true_type{});
+  // max over the 4 lane groups (tokens 4g..4g+3 of each tile)
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  return bm;
+}
+
+template <int D, bool THUMB>
+__device__ __forceinline__ float score_block(const ScanQuery<D, THUMB>& sq, const u32x4_t (&cw)[4], float scl, int t0,
+                                             int lane) {
+  return score_block_q<D, THUMB>(sq, sq.qa, cw, scl, t0, lane);
+}
+
+template <int D, int G, int QT, bool THUMB, int NW>
+__device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
+                                               int j0, int nblk_split, int nx, int L, int sl, int lane, int w) {
+  constexpr int R = G * QT;
+  const int nblk = nblk_split + nx;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const ScanQuery<D, THUMB> sq = scan_query<D, G, QT, THUMB, NW>(p, sm, sl, lane);
 
   constexpr int kChunk = 4;
   const int rot = scan_rotation(p, j0, nblk_split);
@@ -209,36 +329,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
         int jp = jl + rot;   // the split's blocks in rotated order
         if (jp >= nblk_split) jp -= nblk_split;
         const int jb = jl < nblk_split ? j0 + jp : sm.xidx[jl - nblk_split];
-        const int t0 = jb * kBlockSize;
-        const size_t r0 = block_row(p, sm, b, j, j0, nblk_split, jb);
-        constexpr int RB = THUMB ? D / 4 : D / 2;   // code bytes per token
-        const uint8_t* kq = (THUMB ? p.k2 : p.kq) + r0 * RB;
-        const float* ks = (THUMB ? p.k2scale : p.kscale) + r0;
-        // The int4 sketch is read once: streaming loads. The thumbnail codes
-        // and scales of a kept block are read again by the attend: ordinary
-        // loads, so that the re-read can hit in L2.
-#pragma unroll
-        for (int T = 0; T < 4; ++T) {
-          const int t = t0 + 16 * T + n;
-          const bool ok = t < L;
-          const uint8_t* src = kq + (size_t)(ok ? t - t0 : 0) * RB + g * (RB / 4);
-          if constexpr (RB / 4 == 16) {
-            cw[c][T] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src)) : u32x4_t{0u, 0u, 0u, 0u};
-          } else if constexpr (RB / 4 == 8) {
-            const u32x2_t* s2 = reinterpret_cast<const u32x2_t*>(src);
-            const u32x2_t u = ok ? (THUMB ? *s2 : __builtin_nontemporal_load(s2)) : u32x2_t{0u, 0u};
-            cw[c][T] = u32x4_t{u.x, u.y, 0u, 0u};
-          } else {
-            const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
-            const uint32_t u = ok ? (THUMB ? *s1 : __builtin_nontemporal_load(s1)) : 0u;
-            cw[c][T] = u32x4_t{u, 0u, 0u, 0u};
-          }
-        }
-        // the 16 scales lane (g, n) needs (tokens 16T + 4g + r) are held by
-        // lanes 4T + r of its own 16-lane row: one load per lane, then row
-        // broadcasts; tokens past the sequence are not read
-        const int tl = 16 * (n >> 2) + 4 * g + (n & 3);
-        scl[c] = t0 + tl < L ? (THUMB ? ks[tl] : __builtin_nontemporal_load(ks + tl)) : 0.f;
+        load_sketch<D, THUMB>(p, block_row(p, sm, b, j, j0, nblk_split, jb), jb * kBlockSize, L, lane, cw[c], scl[c]);
       }
     }
 #pragma unroll
@@ -248,44 +339,7 @@ __device__ __forceinline__ void scan_blocks_mq(const DecodeParams& p, DecodeSmem
       int jp = jl + rot;
       if (jp >= nblk_split) jp -= nblk_split;
       const int t0 = (jl < nblk_split ? j0 + jp : sm.xidx[jl - nblk_split]) * kBlockSize;
-      float bm = -INFINITY;
-      // scores of the block's 4 tiles; MASKED: drop the tokens row n cannot see
-      auto tiles = [&](auto masked) {
-#pragma unroll
-        for (int T = 0; T < 4; ++T) {
-          i32x4_t acc = acc0;
-#pragma unroll
-          for (int s = 0; s < NM; ++s) {
-            i32x4_t kb;
-            if constexpr (THUMB) {
-              const uint32_t x = cw[c][T][s];
-              kb = i32x4_t{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u),
-                           (int)((x >> 6) & 0x03030303u)};
-            } else {
-              // two's complement -> code + 8, low and high nibbles
-              const uint32_t x0 = cw[c][T][2 * s], x1 = cw[c][T][2 * s + 1];
-              kb = i32x4_t{(int)((x0 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x0 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu),
-                           (int)((x1 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x1 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu)};
-            }
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb, qa[s], acc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float wgt = row_bcast_f(scl[c], 4 * T + r) * cq;
-            const int dot = THUMB ? 2 * acc[r] - corr : acc[r];
-            const float sv = (float)dot * wgt;
-            if constexpr (decltype(masked)::value)
-              bm = fmaxf(bm, t0 + 16 * T + 4 * g + r < Lr ? sv : -INFINITY);
-            else
-              bm = fmaxf(bm, sv);
-          }
-        }
-      };
-      if (t0 + kBlockSize <= Lmin) tiles(std::false_type{});
-      else tiles(std::true_type{});
-      // max over the 4 lane groups (tokens 4g..4g+3 of each tile)
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float bm = score_block<D, THUMB>(sq, cw[c], scl[c], t0, lane);
       if (g == 0 && n < R) {
         if (jl < nblk_split) sm.blk[jp][n] = bm;
         else sm.xblk[jl - nblk_split][n] = bm;
@@ -420,38 +474,47 @@ struct AttendState {
 // nonzero weights it drops are below 2^-62 of the row's sum.
 constexpr float kSeedSlack = 64.f;
 
-// Lrow: tokens this lane's row (lane % 16) may see; L: tokens of the sequence
-// (the longest row), which bounds every load.
-// Kept blocks first, first + stride, ... are this wave's; its V tile is the
-// one of wave w of the workgroup.
+// Per-wave constants of the attend phase.
+template <int D>
+struct AttendCtx {
+  bf16x8_t qop[D / 32];   // B operand of QK: the bf16 query of row h = lane % 16
+  int wbase[2];           // LDS addresses of this lane's V-tile stores
+  int rbase, rx;          // LDS address parts of this lane's transposed V reads
+  float zscale;           // sm_scale * log2(e)
+  float qs;               // thumbnail path: sum of the row's bf16 query
+  bool hv;                // lane's row is a row of a real query token
+  char* vt;               // this wave's V tile
+};
+
+// Set up wave w's attend: the query rows as the QK B operand, the V tile's
+// addresses, and the softmax state, its running max seeded with seed[h]
+// (natural-log units) unless DENSE. Reads the bf16 query rows from LDS, which
+// share their space with the V tiles: the caller must place a workgroup
+// barrier between every wave's set-up and any wave's first block.
 template <int D, int G, int QT, bool DENSE, bool THUMB, int NW>
-__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
-                                              int j0, int L, int Lrow, int lane, int first, int stride,
-                                              AttendState<D>& st) {
-  const int w = first % NW;
+__device__ __forceinline__ void attend_setup(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int lane, int w,
+                                             AttendCtx<D>& c, AttendState<D>& st) {
   constexpr int R = G * QT;
   constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
   constexpr int NT = D / 16;    // MFMA n-tiles of the output
   constexpr int VC = D / 8;     // 16-byte chunks per V row
-  constexpr int VL = 64 * VC / kWave;  // 16-byte V loads per lane per block
   const int h = lane & 15;
   const int g = lane >> 4;
 
-  const bool hv = h < R && h / G < p.Q;   // a row of a real query token
+  c.hv = h < R && h / G < p.Q;   // a row of a real query token
   // B operand of QK: the bf16 query of row h, dims g*D/4 + 8s .. +8 for k-step s
-  bf16x8_t qop[KS];
   {
-    const uint16_t* qh = &sm.qb[hv ? h : 0][g * (D / 4)];
+    const uint16_t* qh = &sm.qb[c.hv ? h : 0][g * (D / 4)];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4_t u = u32x4_t{0u, 0u, 0u, 0u};
       if constexpr (!THUMB) {
-        if (hv) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
+        if (c.hv) u = *reinterpret_cast<const u32x4_t*>(qh + 8 * s);
       } else {
         // thumbnail order (see the QK below): slot 4*kk + m of k-step s is
         // dim 16*(s/2) + 4m + k0 + kk, k0 = 2*(s%2); dword m of that row part
         // holds dims (4m + k0, 4m + k0 + 1)
-        if (hv) {
+        if (c.hv) {
           uint32_t dw[4];
 #pragma unroll
           for (int m = 0; m < 4; ++m)
@@ -460,31 +523,272 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
                       (dw[0] >> 16) | (dw[1] & 0xffff0000u), (dw[2] >> 16) | (dw[3] & 0xffff0000u)};
         }
       }
-      qop[s] = as_bf16x8(u);
+      c.qop[s] = as_bf16x8(u);
     }
   }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) st.o[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  st.m = hv ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
+  st.m = c.hv ? (DENSE ? -INFINITY : sm.seed[h] * kLog2e) : 0.f;
   st.l = 0.f;
   st.fresh = true;
 
-  char* vt = reinterpret_cast<char*>(sm.vt[w]);
+  c.vt = reinterpret_cast<char*>(sm.vt[w]);
   // LDS addresses of the V tile. Store: 16-byte chunk n*64 + lane of the tile
   // goes to wbase[n & 1] + (n >> 1) * 2048 (the row swizzle repeats every 8
   // rows for D=128, and every 2 stores for D=64). Transposed read for k-step
   // ks, half hf, n-tile nt: rbase + 32 rows*ks + 16 rows*hf + ((nt ^ rx) << 5).
   constexpr int ROWB = 2 * D;
   constexpr int RPS = kWave / VC;   // rows per 1 KiB store
-  int wbase[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) wbase[par] = vt_off<D>(par * RPS + lane / VC, lane % VC);
+  for (int par = 0; par < 2; ++par) c.wbase[par] = vt_off<D>(par * RPS + lane / VC, lane % VC);
   const int rr = 4 * g + (h >> 2);
-  const int rx = (D == 128) ? (rr & 7) : ((rr >> 1) & 3);
-  const int rbase = rr * ROWB + ((h & 3) >> 1) * 16 + (h & 1) * 8;
-  const float zscale = p.sm_scale * kLog2e;
+  c.rx = (D == 128) ? (rr & 7) : ((rr >> 1) & 3);
+  c.rbase = rr * ROWB + ((h & 3) >> 1) * 16 + (h & 1) * 8;
+  c.zscale = p.sm_scale * kLog2e;
+  c.qs = (THUMB && c.hv) ? sm.qsumf[h] : 0.f;
+}
+
+// The registers a block's attend loads into.
+template <int D, bool THUMB>
+struct BlockLoads {
+  u32x4_t kr[4][D / 32];                        // bf16 K rows (int4 path)
+  uint32_t kc[4][(D / 64) > 0 ? D / 64 : 1];    // thumbnail codes (16 per word)
+  u32x2_t kres[4][D / 32];                      // residual bytes, 8 per k-step
+  float tsl, s8l;                               // thumbnail and residual scales of row `lane`
+  u32x4_t vr[64 * (D / 8) / kWave];             // V chunks
+};
+
+// Attend one block (first cache row r0, first token t0) for the rows whose
+// bit is set in hm: its K (or thumbnail codes + residuals) and V, QK on the
+// matrix cores, the online softmax, PV. Lrow: tokens this lane's row (lane %
+// 16) may see; L: tokens of the sequence (the longest row), which bounds
+// every load.
+template <int D, int G, int QT, bool THUMB>
+__device__ __forceinline__ void attend_issue(const DecodeParams& p, const AttendCtx<D>& c, size_t r0, int t0, int L,
+                                             int lane, BlockLoads<D, THUMB>& ld) {
+  constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
+  constexpr int VC = D / 8;     // 16-byte chunks per V row
+  constexpr int VL = 64 * VC / kWave;  // 16-byte V loads per lane per block
+  const int h = lane & 15;
+  const int g = lane >> 4;
+  const int tlast = L - 1;   // rows past the sequence are read from its last row and masked
+  const uint16_t* kb = p.k + r0 * D;   // token t of this block is row t - t0
+  const uint16_t* vb = p.v + r0 * D;
+
+  // ---- issue the block's loads: K (or its thumbnail + residual) and V ----
+  auto& kr = ld.kr;
+  auto& kc = ld.kc;
+  auto& kres = ld.kres;
+  float& tsl = ld.tsl;
+  float& s8l = ld.s8l;
+  tsl = 0.f;
+  s8l = 0.f;
+  if constexpr (!THUMB) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int t = min(t0 + 16 * T + h, tlast);
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)(t - t0) * D + g * (D / 4));
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kr[T][s] = src[s];
+    }
+  } else {
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int t = min(t0 + 16 * T + h, tlast);
+      const uint8_t* cs = p.k2 + (r0 + (size_t)(t - t0)) * (D / 4) + g * (D / 16);
+      if constexpr (D == 128) {
+        const u32x2_t u = *reinterpret_cast<const u32x2_t*>(cs);
+        kc[T][0] = u.x;
+        kc[T][1] = u.y;
+      } else {
+        kc[T][0] = *reinterpret_cast<const uint32_t*>(cs);
+      }
+      const u32x2_t* rs = reinterpret_cast<const u32x2_t*>(p.kr + (r0 + (size_t)(t - t0)) * D + g * (D / 4));
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kres[T][s] = __builtin_nontemporal_load(rs + s);   // read once
+    }
+    // per-token scales: lane l holds those of row l of the block
+    const int tl = min(t0 + lane, tlast) - t0;
+    tsl = p.k2scale[r0 + tl];
+    s8l = __builtin_nontemporal_load(p.krscale + r0 + tl);
+  }
+  // The whole V tile is in flight across QK, on the thumbnail path too.
+  // (Loading V straight into LDS with global_load_lds_dwordx4 frees its
+  // registers, but the compiler then waits for every outstanding load, the
+  // V DMA included, before the first use of the codes, which serialises V
+  // behind QK: slower.)
+  auto& vr = ld.vr;
+#pragma unroll
+  for (int n = 0; n < VL; ++n) {
+    const int f = n * kWave + lane;        // chunk id within the tile
+    const int r = f / VC, q = f % VC;
+    const int t = min(t0 + r, tlast);
+    vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)(t - t0) * D + q * 8));
+  }
+
+}
+
+// The compute half: QK, V tile, online softmax, PV of a block whose loads
+// attend_issue put in flight (waiting for them here).
+template <int D, int G, int QT, bool THUMB>
+__device__ __forceinline__ void attend_compute(const AttendCtx<D>& c, AttendState<D>& st, int t0, int Lrow,
+                                               unsigned hm, int lane, const BlockLoads<D, THUMB>& ld) {
+  constexpr int KS = D / 32;    // MFMA k-steps over the head dimension
+  constexpr int NT = D / 16;    // MFMA n-tiles of the output
+  constexpr int VC = D / 8;     // 16-byte chunks per V row
+  constexpr int VL = 64 * VC / kWave;  // 16-byte V loads per lane per block
+  constexpr int ROWB = 2 * D;
+  const int h = lane & 15;
+  const int g = lane >> 4;
+  const auto& kr = ld.kr;
+  const auto& kc = ld.kc;
+  const auto& kres = ld.kres;
+  const float tsl = ld.tsl, s8l = ld.s8l;
+  const auto& vr = ld.vr;
+  // ---- QK on the matrix cores ----
+  const auto& qop = c.qop;
+  f32x4_t sacc[4];
+  if constexpr (!THUMB) {
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      sacc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[T][s]), qop[s], sacc[T], 0, 0, 0);
+    }
+  } else {
+    // q.K^ = t * (2 q.u - 3 sum q) + s8 * q.r8: u and r8 are small integers,
+    // exact in bf16, so both dot products run on the matrix cores exactly up
+    // to fp32 accumulation and K^ is never formed.
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t ar = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // k-step s covers the lane's dims 16*(s/2) + 4m + k0 + kk (m = 0..3,
+      // kk = 0..1, k0 = 2*(s%2)) in slot 4*kk + m: byte m of
+      // (codes >> 2(k0 + kk)) & 0x03030303 is exactly the code of that dim,
+      // so each pair of bf16 codes is two byte permutes from a table; the
+      // residual byte of dim d is byte d%4 of word d/4, read by the convert.
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int k0 = 2 * (s & 1);
+        const uint32_t w = kc[T][s >> 1];
+        const uint32_t y0 = (w >> (2 * k0)) & 0x03030303u;
+        const uint32_t y1 = (w >> (2 * k0 + 2)) & 0x03030303u;
+        const u32x4_t ub = u32x4_t{code_pair_bf16<0x05010400u>(y0), code_pair_bf16<0x07030602u>(y0),
+                                   code_pair_bf16<0x05010400u>(y1), code_pair_bf16<0x07030602u>(y1)};
+        bf16x8_t a_r;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x2_t rw = kres[T][2 * (s >> 1) + (m >> 1)];
+            const uint32_t word = (m & 1) ? rw.y : rw.x;
+            a_r[4 * kk + m] = (__bf16)(float)(int8_t)(word >> (8 * (k0 + kk)));
+          }
+        au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ub), qop[s], au, 0, 0, 0);
+        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_r, qop[s], ar, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int src = 16 * T + 4 * g + r;   // the lane holding this row's scales
+        const float ts = __shfl(tsl, src);
+        const float s8 = __shfl(s8l, src);
+        sacc[T][r] = ts * (2.f * au[r] - 3.f * c.qs) + s8 * ar[r];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // convert tile by tile: bounds live registers
+    }
+  }
+
+  // ---- V tile to LDS (this wave's region) ----
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int n = 0; n < VL; ++n)
+    *reinterpret_cast<u32x4_t*>(c.vt + c.wbase[n & 1] + (n >> 1) * 2048) = vr[n];
+
+  // ---- online softmax in the MFMA output layout ----
+  const bool head_keeps = c.hv && ((hm >> h) & 1u);
+  float sv[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * T + 4 * g + r;
+      const float z = sacc[T][r] * c.zscale;
+      sv[T][r] = (head_keeps && t < Lrow) ? z : -INFINITY;
+      mx = fmaxf(mx, sv[T][r]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // a fresh row takes the block's exact max when the seed lies too far
+  // above it (nothing to rescale: o and l are 0); afterwards m only rises
+  const bool fresh = st.fresh;
+  const bool up = mx > st.m || (fresh && mx != -INFINITY && mx < st.m - kSeedSlack);   // (unseeded: m = -inf)
+  if (mx != -INFINITY) st.fresh = false;
+  if (__ballot(up)) {
+    const float mn = up ? mx : st.m;
+    const float alpha = (st.m == -INFINITY || fresh) ? 0.f : fast_exp2(st.m - mn);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st.o[nt][r] *= ar;
+    }
+  }
+  bf16x8_t phi[2], plo[2];
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pr = (sv[T][r] == -INFINITY) ? 0.f : fast_exp2(sv[T][r] - st.m);
+      st.l += pr;
+      const __bf16 hi = (__bf16)pr;
+      const __bf16 lo = (__bf16)(pr - (float)hi);
+      phi[T >> 1][(T & 1) * 4 + r] = hi;
+      plo[T >> 1][(T & 1) * 4 + r] = lo;
+    }
+
+  // ---- PV on the matrix cores: B = V read transposed from LDS ----
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // providing lane (g, h): row 32ks + 16hf + 4g + h/4, dims 16nt + 4(h%4) .. +4
+      const char* a = c.vt + c.rbase + ks * 32 * ROWB + ((nt ^ c.rx) << 5);
+      const bf16x4_t v0 = lds_read_tr(a);
+      const bf16x4_t v1 = lds_read_tr(a + 16 * ROWB);
+      const bf16x8_t vb8 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[ks], vb8, st.o[nt], 0, 0, 0);
+      st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb8, st.o[nt], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int G, int QT, bool THUMB>
+__device__ __forceinline__ void attend_block(const DecodeParams& p, const AttendCtx<D>& c, AttendState<D>& st,
+                                             size_t r0, int t0, int L, int Lrow, unsigned hm, int lane) {
+  BlockLoads<D, THUMB> ld;
+  attend_issue<D, G, QT, THUMB>(p, c, r0, t0, L, lane, ld);
+  attend_compute<D, G, QT, THUMB>(c, st, t0, Lrow, hm, lane, ld);
+}
+
+// Lrow: tokens this lane's row (lane % 16) may see; L: tokens of the sequence
+// (the longest row), which bounds every load.
+// Kept blocks first, first + stride, ... are this wave's; its V tile is the
+// one of wave w of the workgroup.
+template <int D, int G, int QT, bool DENSE, bool THUMB, int NW>
+__device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
+                                              int j0, int L, int Lrow, int lane, int first, int stride,
+                                              AttendState<D>& st) {
+  AttendCtx<D> c;
+  attend_setup<D, G, QT, DENSE, THUMB, NW>(p, sm, lane, first % NW, c, st);
   const int nkept = sm.nkept;
-  const float qs = (THUMB && hv) ? sm.qsumf[h] : 0.f;
   __syncthreads();   // the query rows share their space with the V tiles
 
   // Kept blocks are taken last-scanned first: on the thumbnail path their
@@ -494,183 +798,8 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
   for (int e0 = first; e0 < nkept; e0 += stride) {
     const int e = nkept - 1 - e0;
     const int jb = j0 + sm.kidx[e];
-    const unsigned hm = sm.khm[e];
-    const int t0 = jb * kBlockSize;
-    const int tlast = L - 1;   // rows past the sequence are read from its last row and masked
     const size_t r0 = block_row(p, sm, b, j, j0, kMaxSplit, jb);   // kept blocks lie in the split
-    const uint16_t* kb = p.k + r0 * D;   // token t of this block is row t - t0
-    const uint16_t* vb = p.v + r0 * D;
-
-    // ---- issue the block's loads: K (or its thumbnail + residual) and V ----
-    u32x4_t kr[4][KS];
-    uint32_t kc[4][(D / 64) > 0 ? D / 64 : 1];   // thumbnail codes (16 per word)
-    u32x2_t kres[4][KS];                          // residual bytes, 8 per k-step
-    float tsl = 0.f, s8l = 0.f;                   // thumbnail and residual scales
-    if constexpr (!THUMB) {
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        const int t = min(t0 + 16 * T + h, tlast);
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kb + (size_t)(t - t0) * D + g * (D / 4));
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kr[T][s] = src[s];
-      }
-    } else {
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        const int t = min(t0 + 16 * T + h, tlast);
-        const uint8_t* cs = p.k2 + (r0 + (size_t)(t - t0)) * (D / 4) + g * (D / 16);
-        if constexpr (D == 128) {
-          const u32x2_t u = *reinterpret_cast<const u32x2_t*>(cs);
-          kc[T][0] = u.x;
-          kc[T][1] = u.y;
-        } else {
-          kc[T][0] = *reinterpret_cast<const uint32_t*>(cs);
-        }
-        const u32x2_t* rs = reinterpret_cast<const u32x2_t*>(p.kr + (r0 + (size_t)(t - t0)) * D + g * (D / 4));
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kres[T][s] = __builtin_nontemporal_load(rs + s);   // read once
-      }
-      // per-token scales: lane l holds those of row l of the block
-      const int tl = min(t0 + lane, tlast) - t0;
-      tsl = p.k2scale[r0 + tl];
-      s8l = __builtin_nontemporal_load(p.krscale + r0 + tl);
-    }
-    // The whole V tile is in flight across QK, on the thumbnail path too.
-    // (Loading V straight into LDS with global_load_lds_dwordx4 frees its
-    // registers, but the compiler then waits for every outstanding load, the
-    // V DMA included, before the first use of the codes, which serialises V
-    // behind QK: slower.)
-    u32x4_t vr[VL];
-#pragma unroll
-    for (int n = 0; n < VL; ++n) {
-      const int f = n * kWave + lane;        // chunk id within the tile
-      const int r = f / VC, q = f % VC;
-      const int t = min(t0 + r, tlast);
-      vr[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (size_t)(t - t0) * D + q * 8));
-    }
-
-    // ---- QK on the matrix cores ----
-    f32x4_t sacc[4];
-    if constexpr (!THUMB) {
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        sacc[T] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[T][s]), qop[s], sacc[T], 0, 0, 0);
-      }
-    } else {
-      // q.K^ = t * (2 q.u - 3 sum q) + s8 * q.r8: u and r8 are small integers,
-      // exact in bf16, so both dot products run on the matrix cores exactly up
-      // to fp32 accumulation and K^ is never formed.
-#pragma unroll
-      for (int T = 0; T < 4; ++T) {
-        f32x4_t au = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        f32x4_t ar = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        // k-step s covers the lane's dims 16*(s/2) + 4m + k0 + kk (m = 0..3,
-        // kk = 0..1, k0 = 2*(s%2)) in slot 4*kk + m: byte m of
-        // (codes >> 2(k0 + kk)) & 0x03030303 is exactly the code of that dim,
-        // so each pair of bf16 codes is two byte permutes from a table; the
-        // residual byte of dim d is byte d%4 of word d/4, read by the convert.
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const int k0 = 2 * (s & 1);
-          const uint32_t w = kc[T][s >> 1];
-          const uint32_t y0 = (w >> (2 * k0)) & 0x03030303u;
-          const uint32_t y1 = (w >> (2 * k0 + 2)) & 0x03030303u;
-          const u32x4_t ub = u32x4_t{code_pair_bf16<0x05010400u>(y0), code_pair_bf16<0x07030602u>(y0),
-                                     code_pair_bf16<0x05010400u>(y1), code_pair_bf16<0x07030602u>(y1)};
-          bf16x8_t a_r;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const u32x2_t rw = kres[T][2 * (s >> 1) + (m >> 1)];
-              const uint32_t word = (m & 1) ? rw.y : rw.x;
-              a_r[4 * kk + m] = (__bf16)(float)(int8_t)(word >> (8 * (k0 + kk)));
-            }
-          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ub), qop[s], au, 0, 0, 0);
-          ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_r, qop[s], ar, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int src = 16 * T + 4 * g + r;   // the lane holding this row's scales
-          const float ts = __shfl(tsl, src);
-          const float s8 = __shfl(s8l, src);
-          sacc[T][r] = ts * (2.f * au[r] - 3.f * qs) + s8 * ar[r];
-        }
-        __builtin_amdgcn_sched_barrier(0);   // convert tile by tile: bounds live registers
-      }
-    }
-
-    // ---- V tile to LDS (this wave's region) ----
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int n = 0; n < VL; ++n)
-      *reinterpret_cast<u32x4_t*>(vt + wbase[n & 1] + (n >> 1) * 2048) = vr[n];
-
-    // ---- online softmax in the MFMA output layout ----
-    const bool head_keeps = hv && ((hm >> h) & 1u);
-    float sv[4][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 16 * T + 4 * g + r;
-        const float z = sacc[T][r] * zscale;
-        sv[T][r] = (head_keeps && t < Lrow) ? z : -INFINITY;
-        mx = fmaxf(mx, sv[T][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // a fresh row takes the block's exact max when the seed lies too far
-    // above it (nothing to rescale: o and l are 0); afterwards m only rises
-    const bool fresh = st.fresh;
-    const bool up = mx > st.m || (!DENSE && fresh && mx != -INFINITY && mx < st.m - kSeedSlack);
-    if (mx != -INFINITY) st.fresh = false;
-    if (__ballot(up)) {
-      const float mn = up ? mx : st.m;
-      const float alpha = (st.m == -INFINITY || fresh) ? 0.f : fast_exp2(st.m - mn);
-      st.m = mn;
-      st.l *= alpha;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * g + r);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st.o[nt][r] *= ar;
-      }
-    }
-    bf16x8_t phi[2], plo[2];
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = (sv[T][r] == -INFINITY) ? 0.f : fast_exp2(sv[T][r] - st.m);
-        st.l += pr;
-        const __bf16 hi = (__bf16)pr;
-        const __bf16 lo = (__bf16)(pr - (float)hi);
-        phi[T >> 1][(T & 1) * 4 + r] = hi;
-        plo[T >> 1][(T & 1) * 4 + r] = lo;
-      }
-
-    // ---- PV on the matrix cores: B = V read transposed from LDS ----
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        // providing lane (g, h): row 32ks + 16hf + 4g + h/4, dims 16nt + 4(h%4) .. +4
-        const char* a = vt + rbase + ks * 32 * ROWB + ((nt ^ rx) << 5);
-        const bf16x4_t v0 = lds_read_tr(a);
-        const bf16x4_t v1 = lds_read_tr(a + 16 * ROWB);
-        const bf16x8_t vb8 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[ks], vb8, st.o[nt], 0, 0, 0);
-        st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[ks], vb8, st.o[nt], 0, 0, 0);
-      }
-    }
+    attend_block<D, G, QT, THUMB>(p, c, st, r0, jb * kBlockSize, L, Lrow, sm.khm[e], lane);
   }
 }
 
@@ -681,6 +810,161 @@ __device__ __forceinline__ void attend_blocks(const DecodeParams& p, DecodeSmem<
 __device__ __forceinline__ void store_out(const DecodeParams& p, size_t idx, float v) {
   if (p.out_f32) static_cast<float*>(p.out)[idx] = v;
   else static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(v);
+}
+
+// The query rows of the workgroup to LDS (thread (qr, qk) holds the 16-byte
+// chunk qk of row qr in qw): the bf16 rows, the int8 scan query with its
+// scale cq and code sum, and (thumbnail path) the bf16 row sums.
+template <int D, int G, int QT, bool DENSE, bool THUMB, int NW>
+__device__ __forceinline__ void query_to_lds(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, u32x4_t qw, int qr,
+                                             int qk) {
+  constexpr int R = G * QT;
+  constexpr int QC = D / 8;   // 16-byte chunks per query row
+  if (qr < R) {
+    // row qr's chunks sit in QC consecutive lanes: its reductions stay there
+    *reinterpret_cast<u32x4_t*>(&sm.qb[qr][qk * 8]) = qw;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(qw[e]);
+      x[2 * e + 1] = bf16_hi(qw[e]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = group_max_f<QC>(amax);
+    if constexpr (THUMB) {
+      float fs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fs += x[e];
+      fs = group_sum_f<QC>(fs);
+      if (qk == 0) sm.qsumf[qr] = fs;
+    }
+    if constexpr (!DENSE) {
+      // amax < 2^-120 counts as a zero query: 127/amax would overflow to +inf
+      const bool nz = amax >= 0x1p-120f;
+      int qsum = 0;
+      uint32_t cw[2] = {0u, 0u};
+      if (nz) {
+        const float inv = 127.0f / amax;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float c = rintf(x[e] * inv);
+          c = fminf(fmaxf(c, -127.f), 127.f);
+          const int ci = (int)c;
+          qsum += ci;
+          cw[e >> 2] |= (uint32_t)(uint8_t)(int8_t)ci << (8 * (e & 3));
+        }
+      }
+      *reinterpret_cast<u32x2_t*>(&sm.qc[qr][qk * 8]) = u32x2_t{cw[0], cw[1]};
+      qsum = group_sum_i<QC>(qsum);
+      if (qk == 0) {
+        sm.sumq[qr] = qsum;
+        sm.cq[qr] = nz ? (amax / 127.0f) * p.sm_scale : 0.f;
+      }
+    }
+  }
+}
+
+// This wave's softmax state to LDS for the workgroup's merge: the
+// normaliser of row h summed over its 4 lane groups, the running max and the
+// unnormalised outputs (which overwrite the V tiles: every wave must be done
+// attending before any wave calls this).
+template <int D, int R, int NW>
+__device__ __forceinline__ void wave_state_to_lds(DecodeSmem<D, R, NW>& sm, const AttendState<D>& st, int lane,
+                                                  int w) {
+  float lw = st.l;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 4 * g + r;
+      if (hh < R) {
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) sm.wo[w][hh][16 * nt + (lane & 15)] = st.o[nt][r];
+      }
+    }
+    if (lane < R) {
+      sm.wm[w][lane] = st.m;
+      sm.wl[w][lane] = lw;
+    }
+  }
+}
+
+// Merge the waves' states (after wave_state_to_lds and a barrier) and write
+// the part's normalised output and natural-log LSE for every row.
+template <int D, int G, int QT, int NW>
+__device__ __forceinline__ void write_partial(const DecodeParams& p, DecodeSmem<D, G * QT, NW>& sm, int b, int j,
+                                              int split, int part, int tid) {
+  constexpr int R = G * QT;
+  constexpr int kThreads = 64 * NW;
+  // ---- epilogue: merge waves, write the split partial -------------------
+  // per row, once: the waves' weights exp2(m_w - m) / den and the LSE
+  if (tid < R) {
+    const int h = tid;
+    // a wave that accumulated nothing for the row (its m may still be the
+    // seed, above every exact logit) takes no part in the merge
+    float wmv[NW];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      wmv[ww] = sm.wl[ww][h] > 0.f ? sm.wm[ww][h] : -INFINITY;
+      mx = fmaxf(mx, wmv[ww]);
+    }
+    float a[NW], den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      a[ww] = (wmv[ww] == -INFINITY) ? 0.f : exp2f(wmv[ww] - mx);
+      den += sm.wl[ww][h] * a[ww];
+    }
+    // a row can keep no block of a split (sink/local pseudo-max, or a query
+    // token that does not see the split): empty partial, weight 0
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) sm.wa[ww][h] = den > 0.f ? a[ww] / den : 0.f;
+    sm.rlse[h] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+  constexpr int D4 = D / 4;
+  for (int i = tid; i < R * D4; i += kThreads) {
+    const int h = i / D4, cc = (i % D4) * 4;
+    if (h / G >= p.Q) continue;
+    f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sm.wo[ww][h][cc]);
+      const float a = sm.wa[ww][h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += x[e] * a;
+    }
+    const size_t row = (row_index<G>(p, b, j, h) * p.n_splits + split) * p.split_parts + part;
+    *reinterpret_cast<f32x4_t*>(p.o_part + row * D + cc) = o;
+    if (cc == 0) p.lse_part[row] = sm.rlse[h];
+  }
+}
+
+// The split's mask entries from the per-block row bits in sm.hmb (blocks past
+// the sequence are 0), four per thread.
+template <int D, int G, int QT, int NW>
+__device__ __forceinline__ void write_mask(const DecodeParams& p, const DecodeSmem<D, G * QT, NW>& sm, int b, int j,
+                                           int j0, int nmask, int tid) {
+  constexpr int R = G * QT;
+  constexpr int kThreads = 64 * NW;
+  const int n4 = (nmask + 3) / 4;
+  for (int i = tid; i < R * n4; i += kThreads) {
+    const int r = i / n4, c = 4 * (i % n4);
+    if (r / G >= p.Q) continue;
+    uint8_t* dst = p.mask + row_index<G>(p, b, j, r) * p.nb_max + j0 + c;
+    uint32_t m4 = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m4 |= (uint32_t)((sm.hmb[min(c + e, kMaxSplit - 1)] >> r) & 1u) << (8 * e);
+    if (c + 4 <= nmask && ((uintptr_t)dst & 3u) == 0) {
+      *reinterpret_cast<uint32_t*>(dst) = m4;
+    } else {
+      for (int e = 0; e < 4 && c + e < nmask; ++e) dst[e] = (uint8_t)(m4 >> (8 * e));
+    }
+  }
 }
 
 // One workgroup per (split, kv head j, sequence b) serving R = G x QT query
@@ -756,50 +1040,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
       if (jb < j0 || jb >= j0 + nblk) sm.xidx[nx++] = jb;
     sm.nx = nx;
   }
-  if (qr < R) {
-    // row qr's chunks sit in QC consecutive lanes: its reductions stay there
-    *reinterpret_cast<u32x4_t*>(&sm.qb[qr][qk * 8]) = qw;
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(qw[e]);
-      x[2 * e + 1] = bf16_hi(qw[e]);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = group_max_f<QC>(amax);
-    if constexpr (THUMB) {
-      float fs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fs += x[e];
-      fs = group_sum_f<QC>(fs);
-      if (qk == 0) sm.qsumf[qr] = fs;
-    }
-    if constexpr (!DENSE) {
-      // amax < 2^-120 counts as a zero query: 127/amax would overflow to +inf
-      const bool nz = amax >= 0x1p-120f;
-      int qsum = 0;
-      uint32_t cw[2] = {0u, 0u};
-      if (nz) {
-        const float inv = 127.0f / amax;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float c = rintf(x[e] * inv);
-          c = fminf(fmaxf(c, -127.f), 127.f);
-          const int ci = (int)c;
-          qsum += ci;
-          cw[e >> 2] |= (uint32_t)(uint8_t)(int8_t)ci << (8 * (e & 3));
-        }
-      }
-      *reinterpret_cast<u32x2_t*>(&sm.qc[qr][qk * 8]) = u32x2_t{cw[0], cw[1]};
-      qsum = group_sum_i<QC>(qsum);
-      if (qk == 0) {
-        sm.sumq[qr] = qsum;
-        sm.cq[qr] = nz ? (amax / 127.0f) * p.sm_scale : 0.f;
-      }
-    }
-  }
+  query_to_lds<D, G, QT, DENSE, THUMB, NW>(p, sm, qw, qr, qk);
   __syncthreads();
 
   // ---- scan + select ------------------------------------------------------
@@ -837,85 +1078,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // this wave's partial: normaliser of row h summed over its 4 lane groups;
   // the partial outputs overwrite the V tiles, so every wave must be done
   __syncthreads();
-  float lw = st.l;
-  lw += __shfl_xor(lw, 16);
-  lw += __shfl_xor(lw, 32);
-  {
-    const int g = lane >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 4 * g + r;
-      if (hh < R) {
-#pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) sm.wo[w][hh][16 * nt + (lane & 15)] = st.o[nt][r];
-      }
-    }
-    if (lane < R) {
-      sm.wm[w][lane] = st.m;
-      sm.wl[w][lane] = lw;
-    }
-  }
+  wave_state_to_lds<D, R, NW>(sm, st, lane, w);
   __syncthreads();
-
-  // ---- epilogue: merge waves, write the split partial -------------------
-  // per row, once: the waves' weights exp2(m_w - m) / den and the LSE
-  if (tid < R) {
-    const int h = tid;
-    // a wave that accumulated nothing for the row (its m may still be the
-    // seed, above every exact logit) takes no part in the merge
-    float wmv[NW];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      wmv[ww] = sm.wl[ww][h] > 0.f ? sm.wm[ww][h] : -INFINITY;
-      mx = fmaxf(mx, wmv[ww]);
-    }
-    float a[NW], den = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      a[ww] = (wmv[ww] == -INFINITY) ? 0.f : exp2f(wmv[ww] - mx);
-      den += sm.wl[ww][h] * a[ww];
-    }
-    // a row can keep no block of a split (sink/local pseudo-max, or a query
-    // token that does not see the split): empty partial, weight 0
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) sm.wa[ww][h] = den > 0.f ? a[ww] / den : 0.f;
-    sm.rlse[h] = den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  constexpr int D4 = D / 4;
-  for (int i = tid; i < R * D4; i += kThreads) {
-    const int h = i / D4, cc = (i % D4) * 4;
-    if (h / G >= p.Q) continue;
-    f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sm.wo[ww][h][cc]);
-      const float a = sm.wa[ww][h];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] += x[e] * a;
-    }
-    const size_t row = (row_index<G>(p, b, j, h) * p.n_splits + split) * p.split_parts + part;
-    *reinterpret_cast<f32x4_t*>(p.o_part + row * D + cc) = o;
-    if (cc == 0) p.lse_part[row] = sm.rlse[h];
-  }
-  // the split's mask entries (blocks past the sequence are 0), four per thread
-  if (p.mask != nullptr && part == 0) {
-    const int n4 = (nmask + 3) / 4;
-    for (int i = tid; i < R * n4; i += kThreads) {
-      const int r = i / n4, c = 4 * (i % n4);
-      if (r / G >= p.Q) continue;
-      uint8_t* dst = p.mask + row_index<G>(p, b, j, r) * p.nb_max + j0 + c;
-      uint32_t m4 = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) m4 |= (uint32_t)((sm.hmb[min(c + e, kMaxSplit - 1)] >> r) & 1u) << (8 * e);
-      if (c + 4 <= nmask && ((uintptr_t)dst & 3u) == 0) {
-        *reinterpret_cast<uint32_t*>(dst) = m4;
-      } else {
-        for (int e = 0; e < 4 && c + e < nmask; ++e) dst[e] = (uint8_t)(m4 >> (8 * e));
-      }
-    }
-  }
+  write_partial<D, G, QT, NW>(p, sm, b, j, split, part, tid);
+  if (p.mask != nullptr && part == 0) write_mask<D, G, QT, NW>(p, sm, b, j, j0, nmask, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1007,10 +1173,11 @@ hipError_t launch_fused(const DecodeParams& p, Stage stage, hipStream_t stream) 
   if ((static_cast<int>(stage) & static_cast<int>(Stage::kPartials)) && p.n_splits > 0) {
     const int gx = p.split_parts == 1 ? p.n_splits : (p.n_splits + 7) / 8 * 8 * p.split_parts;
     dim3 grid(gx, p.Hkv, p.B);
-    if (p.waves == 8)
+    if (p.waves == 8) {
       fused_decode_kernel<D, G, QT, DENSE, THUMB, 8><<<grid, 512, 0, stream>>>(p);
-    else
+    } else {
       fused_decode_kernel<D, G, QT, DENSE, THUMB, 4><<<grid, 256, 0, stream>>>(p);
+    }
   }
   if (static_cast<int>(stage) & static_cast<int>(Stage::kCombine)) {
     combine_kernel<D><<<dim3(p.Q * p.Hq, p.B, D / kCombineDims), kCombineThreads, 0, stream>>>(p);
