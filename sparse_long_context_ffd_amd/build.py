@@ -10,6 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libffd.so")
+SAN_LIB = os.path.join(PKG, "libffd_san.so")   # host layer with AddressSanitizer + UBSan (CPU tests)
 SOURCES = ["ffd_api.hip", "ffd_quantize.hip", "ffd_decode.hip"]
 
 HIPCC_FLAGS = [
@@ -88,5 +89,59 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     return LIB
 
 
+# Host-only sanitizer flags: each -fsanitize applies to the host pass alone
+# (device code is not instrumented); UBSan traps nothing, it reports and the
+# runtime's halt_on_error decides.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_UNITS = ("ffd_api.hip", "ffd_quantize.hip")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to LD_PRELOAD into Python)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return res.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """``libffd_san.so``: the C-ABI host layer (argument validation, dispatch,
+    workspace carving; ffd_api.hip and ffd_quantize.hip) built with
+    AddressSanitizer and UBSan on the host, linked with the decode kernels
+    of the ordinary build (their objects are reused when present)."""
+    objdir = os.path.join(PKG, "_build")
+    units = _units()
+    if not all(os.path.exists(os.path.join(objdir, u[2])) for u in units if u[0] not in SAN_UNITS):
+        build(verbose=verbose)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + SAN_FLAGS
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = []
+    for src, defs, obj in units:
+        if src in SAN_UNITS:
+            out = os.path.join(objdir, "san_" + obj)
+            cmd = [hipcc(), *flags, *inc, *defs, "-c", os.path.join(CSRC, src), "-o", out]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError("hipcc failed building the sanitized host layer")
+            objs.append(out)
+        else:
+            objs.append(os.path.join(objdir, obj))
+    tmp = SAN_LIB + ".tmp"
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libsan", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed linking libffd_san.so")
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))

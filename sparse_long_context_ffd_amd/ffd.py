@@ -26,7 +26,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libffd.so")
+# FFD_LIBRARY selects another build of the same library (the sanitizer build
+# of the host layer, for the CPU tests); it must exist like the default one.
+LIB_PATH = os.environ.get("FFD_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libffd.so")
 
 FFD_OK = 0
 FFD_ERR_INVALID_ARG = 1
