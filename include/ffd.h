@@ -32,7 +32,9 @@
 extern "C" {
 #endif
 
-#define FFD_ABI_VERSION 1
+/* 1: the first release; 2: adds ffd_decode_noalloc (every version-1 call is
+ * unchanged). */
+#define FFD_ABI_VERSION 2
 
 typedef enum {
   FFD_OK = 0,
@@ -44,6 +46,8 @@ typedef enum {
 } ffd_status;
 
 typedef enum { FFD_OUT_BF16 = 0, FFD_OUT_F32 = 1 } ffd_out_dtype;
+/* The same values under the names a plain "dtype" enum would use. */
+typedef enum { FFD_BF16 = FFD_OUT_BF16, FFD_F32 = FFD_OUT_F32 } ffd_dtype;
 
 /* How the pseudo-max m~ of the Top-δ rule is estimated ([TS] Methodology 2). */
 typedef enum {

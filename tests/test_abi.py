@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     exported = set(re.findall(r"\b(ffd_[a-z_0-9]+)\b", dyn))
     assert set(names) <= exported
     assert set(ffd.EXPORTED_SYMBOLS) == set(names)
-    assert ffd.ffd_abi_version() == 1
+    assert ffd.ffd_abi_version() == 2
 
 
 def test_workspace_bytes():
