@@ -158,6 +158,12 @@ def write_summaries(args) -> int:
     traffic = None
     if "dram_read_bytes" in kb and "dram_write_bytes" in kb:
         traffic = int(round(kb["dram_read_bytes"] + kb["dram_write_bytes"]))
+    # cross-check: FETCH_SIZE and WRITE_SIZE scaled by what they read on the
+    # copy of known size
+    fw = None
+    if copy and "fetch_size_kib" in kb and "write_size_kib" in kb and "fetch_size_over_known" in copy:
+        fw = int(round(kb["fetch_size_kib"] * 1024 / copy["fetch_size_over_known"]
+                       + kb["write_size_kib"] * 1024 / copy["write_size_over_known"]))
     cfg = rec["config"]
     out = {
         "kernel": FUSED,
@@ -174,6 +180,7 @@ def write_summaries(args) -> int:
         "traffic_bytes_per_launch": traffic,
         "algorithmic_bytes_per_launch": alg,
         "traffic_over_algorithmic": None if traffic is None else round(traffic / alg, 4),
+        "traffic_fetch_write_size_scaled": fw,
         "flush": rec["timing_us"]["flush"],
         "commands": [c for c in pmc_cmds.splitlines() if c.strip()],
     }
@@ -200,6 +207,9 @@ def write_summaries(args) -> int:
                   f"{fmt(cbd['fetch_size_kib'] * 1024) if 'fetch_size_kib' in cbd else '—'} |")
     md += ["", f"Traffic (DRAM reads + writes) per launch: {fmt(traffic)}; algorithmic bytes {alg / 1e9:.4f} GB; "
                f"traffic / algorithmic = {out['traffic_over_algorithmic']}.",
+           f"Cross-check: FETCH_SIZE and WRITE_SIZE, each scaled by what it reads on the copy of known size "
+           f"(x{1 / copy['fetch_size_over_known']:.4f} and x{1 / copy['write_size_over_known']:.4f}): "
+           f"{fmt(fw)}." if fw is not None else "",
            f"Timed steps in bench.py: {out['flush']}.",
            f"Kernel source hash {rec['kernel_source_hash']}; {k['dispatches']} dispatches averaged.", ""]
     with open(os.path.join(PROFILE_DIR, stem + "_pmc.md"), "w") as f:
