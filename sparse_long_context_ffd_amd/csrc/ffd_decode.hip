@@ -254,11 +254,12 @@ __device__ __forceinline__ void load_sketch(const DecodeParams& p, size_t r0, in
   scl = t0 + tl < L ? (THUMB ? ks[tl] : __builtin_nontemporal_load(ks + tl)) : 0.f;
 }
 
-// score_block with the B operand given by pointer (registers, or LDS where
-// the caller cannot spare the registers).
-template <int D, bool THUMB, typename QA>
-__device__ __forceinline__ float score_block_q(const ScanQuery<D, THUMB>& sq, QA qa, const u32x4_t (&cw)[4], float scl,
-                                               int t0, int lane) {
+// The block's score for row n = lane % 16 from its sketch registers, in every
+// lane of the row: the max over the tokens the row sees of
+// fl32(float(dot) * fl32(scale * cq)).
+template <int D, bool THUMB>
+__device__ __forceinline__ float score_block(const ScanQuery<D, THUMB>& sq, const u32x4_t (&cw)[4], float scl, int t0,
+                                             int lane) {
   constexpr int NM = D / 64;
   const int g = lane >> 4;
   float bm = -INFINITY;
@@ -280,7 +281,7 @@ __device__ __forceinline__ float score_block_q(const ScanQuery<D, THUMB>& sq, QA
           kb = i32x4_t{(int)((x0 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x0 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu),
                        (int)((x1 ^ 0x88888888u) & 0x0f0f0f0fu), (int)(((x1 >> 4) ^ 0x08080808u) & 0x0f0f0f0fu)};
         }
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb, qa[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(kb, sq.qa[s], acc, 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -300,12 +301,6 @@ __device__ __forceinline__ float score_block_q(const ScanQuery<D, THUMB>& sq, QA
   bm = fmaxf(bm, __shfl_xor(bm, 16));
   bm = fmaxf(bm, __shfl_xor(bm, 32));
   return bm;
-}
-
-template <int D, bool THUMB>
-__device__ __forceinline__ float score_block(const ScanQuery<D, THUMB>& sq, const u32x4_t (&cw)[4], float scl, int t0,
-                                             int lane) {
-  return score_block_q<D, THUMB>(sq, sq.qa, cw, scl, t0, lane);
 }
 
 template <int D, int G, int QT, bool THUMB, int NW>
