@@ -983,7 +983,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
   // ragged lengths a fixed split -> x map loads the XCDs that get the low
   // splits more; rotating each (sequence, kv head)'s splits by a different
   // amount spreads every split index over all XCDs.
-  if (p.split_parts == 1) split = (split + b * p.Hkv + j) % p.n_splits;
+  if (p.split_parts == 1) split = (int)(((long)split + (long)b * p.Hkv + j) % p.n_splits);
   if (p.split_parts > 1) {
     // The P workgroups of a split get linear ids 8 apart (the x extent is a
     // multiple of 8), which the dispatcher, dealing workgroups round-robin
