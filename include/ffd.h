@@ -313,7 +313,8 @@ ffd_status ffd_decode_thumb(const void* q, const uint8_t* k2, const float* k2sca
  *   P        = clamp(floor(1024 / units), 1, 4) if units <= 1024, else 1:
  *              workgroups per split when the grid alone would leave the
  *              chip idle; each scans and selects the whole split (one kept
- *              set) and attends every P-th kept block
+ *              set) and attends a disjoint share of its kept blocks (the
+ *              P * waves waves of the split take them round-robin)
  *   o_part   f32 [B, Hq, n_splits, P, d] at byte offset 0: each part's
  *            attention output, normalised over the kept tokens it attended
  *   lse_part f32 [B, Hq, n_splits, P] at byte offset

@@ -11,8 +11,8 @@
 // consecutive 64-token blocks of one (sequence b, kv head j) and serves all
 // G = Hq/Hkv query heads of the group -- for Q query tokens per sequence,
 // G x Q query rows -- so every K/V byte it reads is shared by all of them. When the grid is too small to fill
-// the chip, P workgroups share a split (each scans and selects all of it and
-// attends every P-th kept block).
+// the chip, P workgroups share a split (each scans and selects all of it; the
+// P x 8 waves of the split take its kept blocks round-robin).
 //
 //  prologue  the query rows -> LDS (one 16-byte load per thread): the bf16
 //            rows and the int8 copy + per-row scale (the scan query), reduced

@@ -26,8 +26,9 @@ inline int waves_for(int B, int Hq, int n_splits) {
 
 // Workgroups per split. When (sequence, kv head, split) units are too few to
 // fill the chip, P workgroups share a split: each scans and selects the whole
-// split (same kept set) and attends every P-th kept block, leaving one
-// partial each. A function of (B, Hq, n_splits) alone, so the workspace size
+// split (same kept set) and attends a disjoint share of its kept blocks (the
+// P * waves waves of the split take them round-robin), leaving one partial
+// each. A function of (B, Hq, n_splits) alone, so the workspace size
 // and a separate combine call agree with the decode.
 inline int split_parts_for(int B, int Hq, int n_splits) {
   const long units = (long)B * Hq * n_splits;
