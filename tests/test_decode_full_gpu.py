@@ -1,6 +1,9 @@
-"""Full-size workloads (128K x4, 256K, mixed 8K-128K x16) in the launch
-configuration the benchmark times: the whole kept-block mask bit-exact
-against the oracle, output and LSE within the bar on every head."""
+"""Full-size workloads (128K x4, 256K, mixed 8K-128K x16, and the peaked
+256K diagnostic) in the launch configuration the benchmark times: the whole
+kept-block mask bit-exact against the oracle, output and LSE within the bar
+on every head. Also the skip path's benchmark lines (256K at low delta),
+where most blocks are dropped and the kept counts differ from split to
+split."""
 
 import numpy as np
 import pytest
@@ -14,15 +17,15 @@ from tests.gpu_util import assert_close, assert_mask_equal, run_gpu, say, sm_sca
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_128k_b4", "llama3_8b_256k", "mixed_16x8k_128k"])
-def test_full_size(name):
+def _check_workload(name, deltas):
     w = WORKLOADS[name]
     say(f"full-size workload {name}: generating")
     inp = make_inputs(w)
     dv = to_device(inp)
     sm = sm_scale_for(w.d)
     kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
-    for delta in w.deltas:
+    keeps = []
+    for delta in deltas:
         say(f"  {name} delta={delta}: GPU")
         out, lse, mask = run_gpu(dv, max_seq_len=inp["cap"], delta=delta, sink=w.sink, local=w.local,
                                  split_blocks=w.split_blocks, sm_scale=sm, kq=kq, kscale=ks)
@@ -33,6 +36,20 @@ def test_full_size(name):
         assert_mask_equal(mask, r_mask, f"{name} mask delta={delta}")
         assert_close(out, r_out, f"{name} out delta={delta}")
         assert_close(lse, r_lse, f"{name} lse delta={delta}")
+        keeps.append(float(mask.mean()))
+    return keeps
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_128k_b4", "llama3_8b_256k", "mixed_16x8k_128k", "diag_256k_peaked"])
+def test_full_size(name):
+    _check_workload(name, WORKLOADS[name].deltas)
+
+
+def test_skip_path_low_delta():
+    """256K at the deltas of the skip-path measurements: per-head keeps of
+    about 0.07 to 0.4, kept counts from 1 to 17 blocks per split."""
+    keeps = _check_workload("llama3_8b_256k", (0.25, 0.5, 1.0))
+    assert keeps[0] < 0.15 and keeps[0] < keeps[1] < keeps[2] < 0.5, keeps
 
 
 @pytest.fixture(scope="module")
