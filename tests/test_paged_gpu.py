@@ -89,6 +89,67 @@ def test_paged_equals_contiguous(B, Hq, Hkv, d, lens, delta, pm, S):
     assert_close(outs[1][1], r_lse, "paged lse")
 
 
+def test_shared_prefix_pages():
+    """Sequences that share a prompt prefix share its pages, as a serving
+    cache with prefix reuse holds them: sequences 1 and 2 copy the first 40
+    blocks of sequence 0 and their block tables point at sequence 0's pages
+    for them. Each later sequence quantises only its own tokens (the prefix's
+    sketch is already in the shared pages). Decode over the pool equals the
+    contiguous decode of the same rows bit for bit, and the oracle."""
+    B, Hq, Hkv, d, S, P = 3, 16, 4, 128, 16, 40
+    lens = (6000, 4100, 2600 + 1)   # all longer than the 40-block (2560-token) prefix
+    say(f"paged shared prefix: lens={lens}, {P} shared blocks")
+    inp = make_random_inputs(B, Hq, Hkv, d, lens, seed=931, block_size=64)
+    pre = 64 * P
+    for b in (1, 2):
+        inp["k"][b, :, :pre] = inp["k"][0, :, :pre]
+        inp["v"][b, :, :pre] = inp["v"][0, :, :pre]
+    dv = to_device(inp)
+    cap = inp["cap"]
+    nbs = [-(-L // 64) for L in lens]
+    own = [nbs[0]] + [n - P for n in nbs[1:]]
+    num_pages = sum(own) + 3
+    perm = np.random.default_rng(932).permutation(num_pages)
+    stride = cap // 64 + 1
+    table_np = np.full((B, stride), -3, dtype=np.int32)
+    table_np[0, :nbs[0]] = perm[:nbs[0]]
+    used = nbs[0]
+    for b in (1, 2):
+        table_np[b, :P] = table_np[0, :P]
+        table_np[b, P:nbs[b]] = perm[used:used + own[b]]
+        used += own[b]
+    table = torch.from_numpy(table_np).cuda()
+    k_pages = _paginate(dv["k"], lens, table_np, num_pages, float("nan"))
+    v_pages = _paginate(dv["v"], lens, table_np, num_pages, float("nan"))
+    kq_pages = torch.full((num_pages, Hkv, 64, d // 2), 0xCD, dtype=torch.uint8, device="cuda")
+    ks_pages = torch.full((num_pages, Hkv, 64), float("nan"), dtype=torch.float32, device="cuda")
+    begin = torch.tensor([0, pre, pre], dtype=torch.int32, device="cuda")
+    ffd.ffd_quantize_kv_paged(k_pages, kq_pages, ks_pages, table, begin, dv["seq_lens"], cap)
+    kq, ks = ffd.quantize_kv(dv["k"], dv["seq_lens"])
+    sm = sm_scale_for(d)
+    kw = dict(max_seq_len=cap, block_size=64, delta=1.5, sink=1, local=2, split_blocks=S, sm_scale=sm)
+    res = []
+    for paged in (False, True):
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        mask = torch.empty((B, Hq, -(-cap // 64)), dtype=torch.uint8, device="cuda")
+        ws = ffd.alloc_workspace(B, Hq, d, cap, 64, S)
+        if paged:
+            ffd.ffd_decode_paged(dv["q"], k_pages, v_pages, kq_pages, ks_pages, table, dv["seq_lens"], out=out,
+                                 lse=lse, kept_mask=mask, workspace=ws, **kw)
+        else:
+            ffd.ffd_decode(dv["q"], dv["k"], dv["v"], kq, ks, dv["seq_lens"], out=out, lse=lse, kept_mask=mask,
+                           workspace=ws, **kw)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), lse.cpu().numpy(), mask.cpu().numpy()))
+    for a, b_ in zip(res[0], res[1]):
+        np.testing.assert_array_equal(a, b_)
+    r_out, r_lse, r_mask = O.decode(inp["q"], inp["k"], inp["v"], inp["seq_lens"], **{**kw, "sm_scale": np.float32(sm)})
+    assert_mask_equal(res[1][2], r_mask, "shared prefix mask")
+    assert_close(res[1][0], r_out, "shared prefix out")
+    assert_close(res[1][1], r_lse, "shared prefix lse")
+
+
 def test_paged_dense_path():
     say("paged dense (delta = inf)")
     inp = make_random_inputs(2, 8, 2, 128, (700, 129), seed=5, block_size=64)
