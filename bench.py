@@ -100,26 +100,42 @@ def algorithmic_bytes(mask, seq_lens, Hkv: int, G: int, d: int, bs: int, dense: 
     return scan, kv, (kept_union / blocks if blocks else 0.0)
 
 
-def profile_stem(workload: str, storage: str) -> str:
-    """File stem of the committed rocprofv3 summaries for one workload and key storage."""
-    return f"fused_decode_{'thumb_' if storage == 'thumb' else ''}{workload}"
+def profile_stem(workload: str, mode: dict, queries: int = 1) -> str:
+    """File stem of the committed rocprofv3 summaries for one workload and mode
+    (key storage, KV layout, pseudo-max, query tokens); the default mode's
+    stem is ``fused_decode_<workload>``."""
+    stem = f"fused_decode_{'thumb_' if mode['storage'] == 'thumb' else ''}{workload}"
+    if mode.get("paged"):
+        stem += "_paged"
+    if mode.get("pseudo_max", "split") != "split":
+        stem += f"_{mode['pseudo_max']}"
+    if queries > 1:
+        stem += f"_q{queries}"
+    return stem
 
 
-def load_traffic(workload: str, delta: float, mode: dict):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source in the same mode; else None."""
-    path = os.path.join(PROFILE_DIR, profile_stem(workload, mode["storage"]) + "_pmc.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    if rec.get("delta") != (None if math.isinf(delta) else delta):
-        return None
-    if rec.get("mode", {"storage": "int4", "pseudo_max": "split", "paged": False}) != mode:
-        return None
-    return rec.get("traffic_bytes_per_launch")
+def load_traffic(workload: str, delta: float, mode: dict, queries: int = 1):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if one
+    was taken on the current kernel source in the same mode, at the same δ and
+    number of query tokens (the summary of a non-default δ carries it in its
+    stem: ``<stem>_delta<δ>``); else None."""
+    stem = profile_stem(workload, mode, queries)
+    for cand in (f"{stem}_delta{delta:g}", stem):
+        path = os.path.join(PROFILE_DIR, cand + "_pmc.json")
+        if not os.path.exists(path):
+            continue
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source_hash") != kernel_source_hash():
+            continue
+        if rec.get("delta") != (None if math.isinf(delta) else delta):
+            continue
+        if rec.get("mode", {"storage": "int4", "pseudo_max": "split", "paged": False}) != mode:
+            continue
+        if rec.get("query_tokens", 1) != queries:
+            continue
+        return rec.get("traffic_bytes_per_launch")
+    return None
 
 
 def cpu_baseline(inp, w, delta: float, sm_scale, budget_s: float, pseudo_max: str = "split",
@@ -437,11 +453,11 @@ def main() -> int:
     achieved = alg_bytes / (fused_avg * 1e-6) / 1e9
     value = alg_bytes / (step_us_med * 1e-6) / 1e9
 
-    # counter summaries are taken in the default split size, one query token
+    # counter summaries are taken in the workload's own split size
     traffic = None
-    if Q == 1 and w.split_blocks == WORKLOADS[args.workload].split_blocks:
+    if w.split_blocks == WORKLOADS[args.workload].split_blocks:
         traffic = load_traffic(w.name, delta, {"storage": args.storage, "pseudo_max": args.pseudo_max,
-                                               "paged": bool(args.paged)})
+                                               "paged": bool(args.paged)}, Q)
     rec = {
         "metric": METRIC,
         "value": round(value, 1),

@@ -74,10 +74,21 @@ def test_summary_is_consistent_and_current(path):
         "profile taken on another kernel source: re-run the rocprofv3 passes"
 
 
-def test_bench_uses_the_headline_summary():
+def _traffic(stem):
+    return json.load(open(os.path.join(ROOT, "profiles", stem + "_pmc.json")))["traffic_bytes_per_launch"]
+
+
+def test_bench_finds_the_summary_of_its_mode():
+    """Each bench line takes the summary of its own workload, δ, storage, KV
+    layout, pseudo-max and query-token count, and none when there is none."""
     mode = {"storage": "int4", "pseudo_max": "split", "paged": False}
-    t = bench.load_traffic("llama3_8b_128k_b4", 6.0, mode)
-    rec = json.load(open(os.path.join(ROOT, "profiles", "fused_decode_llama3_8b_128k_b4_pmc.json")))
-    assert t == rec["traffic_bytes_per_launch"]
-    assert bench.load_traffic("llama3_8b_128k_b4", 5.0, mode) is None
-    assert bench.load_traffic("llama3_8b_128k_b4", 6.0, {**mode, "paged": True}) is None
+    c3 = "llama3_8b_128k_b4"
+    assert bench.load_traffic(c3, 6.0, mode) == _traffic("fused_decode_llama3_8b_128k_b4")
+    assert bench.load_traffic(c3, 6.0, {**mode, "paged": True}) == _traffic("fused_decode_llama3_8b_128k_b4_paged")
+    assert bench.load_traffic(c3, 6.0, mode, 4) == _traffic("fused_decode_llama3_8b_128k_b4_q4")
+    assert bench.load_traffic(c3, 6.0, {**mode, "pseudo_max": "sink_local"}) == \
+        _traffic("fused_decode_llama3_8b_128k_b4_sink_local")
+    assert bench.load_traffic("llama3_8b_256k", 0.25, mode) == _traffic("fused_decode_llama3_8b_256k_delta0.25")
+    assert bench.load_traffic(c3, 5.0, mode) is None
+    assert bench.load_traffic(c3, 6.0, mode, 2) is None
+    assert bench.load_traffic(c3, 6.0, {**mode, "paged": True, "pseudo_max": "sink_local"}) is None
